@@ -1,0 +1,76 @@
+"""Full non-causal attention, fp64 (oracle; test infrastructure only).
+
+Source: the vidax paper (arXiv 2609.18077), §1 "Spatiotemporal constraints
+in video generation" (full self-attention over all patch tokens of a
+multi-frame latent) and §2 "3D RoPE, 3D VAEs, and flash attention"
+(unmasked attention goes to flash-attention kernels, Dao et al. 2022, which
+give the exact softmax attention without storing the whole score matrix).
+The agihunt.info summary states the same.  The oracle computes the plain
+definition, materialising each score row in full:
+
+    s_j = (q . k_j) * scale            over all N keys
+    p_j = exp(s_j - max s) / sum_j exp(s_j - max s)
+    o   = sum_j p_j v_j
+    lse = max s + ln sum_j exp(s_j - max s)
+
+No mask, no causality, no dropout.  scale defaults to 1 / sqrt(head_dim).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .rope3d import rope3d_apply
+
+
+def softmax_rows(s) -> np.ndarray:
+    """Row-wise softmax of a float64 score matrix (max subtracted first)."""
+    s = np.asarray(s, dtype=np.float64)
+    e = np.exp(s - s.max(axis=-1, keepdims=True))
+    return e / e.sum(axis=-1, keepdims=True)
+
+
+def attention(q, k, v, scale: float = 0.0, rows=None, row_block: int = 512):
+    """Attention outputs for the query rows ``rows`` (default: all).
+
+    q: [N, H, d] (only the rows selected are read), k, v: [N, H, d].
+    Returns (o [R, H, d] float64, lse [H, R] float64), R = len(rows).
+    """
+    n, heads, d = k.shape
+    if scale <= 0.0:
+        scale = 1.0 / np.sqrt(d)
+    rows = np.arange(q.shape[0]) if rows is None else np.asarray(rows, dtype=np.int64)
+    o = np.empty((rows.size, heads, d), dtype=np.float64)
+    lse = np.empty((heads, rows.size), dtype=np.float64)
+    for h in range(heads):
+        kh = np.asarray(k[:, h, :], dtype=np.float64)
+        vh = np.asarray(v[:, h, :], dtype=np.float64)
+        for r0 in range(0, rows.size, row_block):
+            sel = rows[r0:r0 + row_block]
+            qh = np.asarray(q[sel, h, :], dtype=np.float64)
+            s = (qh @ kh.T) * scale                           # [r, N]
+            m = s.max(axis=1, keepdims=True)
+            e = np.exp(s - m)
+            total = e.sum(axis=1, keepdims=True)
+            o[r0:r0 + sel.size, h, :] = (e @ vh) / total
+            lse[h, r0:r0 + sel.size] = m[:, 0] + np.log(total[:, 0])
+    return o, lse
+
+
+def attention_rope(q, k, v, grid, split, theta=10000.0, n_prefix=0, scale=0.0,
+                   rows=None):
+    """RoPE on Q and K, then attention; one head at a time.
+
+    Arguments as in ``attention``; returns (o [R, H, d], lse [H, R]).
+    """
+    n, heads, d = k.shape
+    rows = np.arange(q.shape[0]) if rows is None else np.asarray(rows, dtype=np.int64)
+    o = np.empty((rows.size, heads, d), dtype=np.float64)
+    lse = np.empty((heads, rows.size), dtype=np.float64)
+    for h in range(heads):
+        kr = rope3d_apply(k[:, h:h + 1, :], grid, split, theta, n_prefix)
+        qr = rope3d_apply(q[rows, h:h + 1, :], grid, split, theta, n_prefix, tokens=rows)
+        # attention() indexes q by token, so place the rotated rows at 0..R-1
+        oh, lh = attention(qr, kr, v[:, h:h + 1, :], scale)
+        o[:, h:h + 1, :] = oh
+        lse[h:h + 1, :] = lh
+    return o, lse

@@ -1,0 +1,127 @@
+"""Pins for the attention oracle (CPU only).
+
+The oracle is compared with torch's scaled_dot_product_attention and
+scipy's logsumexp in float64, and with closed forms: equal keys give the
+mean of V, a dominant key selects its value, N = 1 returns V, and joint
+permutations of K/V leave the result unchanged.
+"""
+import numpy as np
+import pytest
+import scipy.special
+import torch
+
+import oracle
+
+
+def _qkv(n=40, h=3, d=64, seed=0):
+    g = np.random.default_rng(seed)
+    return (g.standard_normal((n, h, d)), g.standard_normal((n, h, d)),
+            g.standard_normal((n, h, d)))
+
+
+@pytest.mark.parametrize("n,d", [(1, 64), (37, 64), (130, 128)])
+def test_matches_library_sdpa(n, d):
+    q, k, v = _qkv(n, 3, d)
+    o, _ = oracle.attention(q, k, v)
+    t = lambda a: torch.from_numpy(a).permute(1, 0, 2)[None]          # [1,H,N,d]
+    ref = torch.nn.functional.scaled_dot_product_attention(t(q), t(k), t(v))
+    np.testing.assert_allclose(o, ref[0].permute(1, 0, 2).numpy(), rtol=0, atol=1e-12)
+
+
+def test_explicit_scale_matches_library():
+    q, k, v = _qkv(50, 2, 64, seed=1)
+    o, _ = oracle.attention(q, k, v, scale=0.3)
+    t = lambda a: torch.from_numpy(a).permute(1, 0, 2)[None]
+    ref = torch.nn.functional.scaled_dot_product_attention(t(q), t(k), t(v), scale=0.3)
+    np.testing.assert_allclose(o, ref[0].permute(1, 0, 2).numpy(), rtol=0, atol=1e-12)
+
+
+def test_lse_is_library_logsumexp():
+    q, k, v = _qkv(60, 2, 64, seed=2)
+    _, lse = oracle.attention(q, k, v)
+    for h in range(2):
+        s = q[:, h] @ k[:, h].T / 8.0
+        np.testing.assert_allclose(lse[h], scipy.special.logsumexp(s, axis=1), rtol=0,
+                                   atol=1e-12)
+
+
+def test_softmax_rows_sum_to_one():
+    g = np.random.default_rng(3)
+    p = oracle.softmax_rows(g.standard_normal((20, 300)) * 10)
+    np.testing.assert_allclose(p.sum(axis=1), 1.0, atol=1e-12)
+    assert (p >= 0).all()
+
+
+def test_equal_keys_give_mean_of_values():
+    q, k, v = _qkv(33, 2, 64, seed=4)
+    k[:] = k[0]
+    o, lse = oracle.attention(q, k, v)
+    np.testing.assert_allclose(o, np.broadcast_to(v.mean(axis=0), o.shape), atol=1e-12)
+    # lse = s + ln N for identical scores
+    s = np.einsum("nhd,hd->hn", q, k[0]) / 8.0
+    np.testing.assert_allclose(lse, s + np.log(33), atol=1e-12)
+
+
+def test_dominant_key_selects_its_value():
+    q, k, v = _qkv(25, 2, 64, seed=5)
+    k[11] = 200.0 * q[0]          # huge score for query 0 only
+    o, _ = oracle.attention(q, k, v, rows=[0])
+    np.testing.assert_allclose(o[0], v[11], atol=1e-12)
+
+
+def test_single_token_returns_value():
+    q, k, v = _qkv(1, 4, 128, seed=6)
+    o, lse = oracle.attention(q, k, v)
+    np.testing.assert_allclose(o, v, atol=0)
+
+
+def test_permutation_invariance():
+    q, k, v = _qkv(45, 2, 64, seed=7)
+    perm = np.random.default_rng(8).permutation(45)
+    o1, _ = oracle.attention(q, k, v)
+    o2, _ = oracle.attention(q, k[perm], v[perm])
+    np.testing.assert_allclose(o1, o2, atol=1e-12)
+    o3, _ = oracle.attention(q[perm], k, v)
+    np.testing.assert_allclose(o3, o1[perm], atol=1e-12)
+
+
+def test_shift_invariance_of_scores():
+    # Adding c*q to every key adds c*|q|^2*scale to each score of a row.
+    q, k, v = _qkv(30, 1, 64, seed=9)
+    o1, _ = oracle.attention(q, k, v, rows=[4])
+    o2, _ = oracle.attention(q, k + 0.7 * q[4], v, rows=[4])
+    np.testing.assert_allclose(o1, o2, atol=1e-12)
+
+
+def test_row_subset_matches_full():
+    q, k, v = _qkv(70, 2, 64, seed=10)
+    o, lse = oracle.attention(q, k, v)
+    rows = np.array([0, 13, 69])
+    o2, lse2 = oracle.attention(q, k, v, rows=rows, row_block=2)
+    np.testing.assert_allclose(o2, o[rows], rtol=0, atol=1e-14)
+    np.testing.assert_allclose(lse2, lse[:, rows], rtol=0, atol=1e-14)
+
+
+def test_rope_then_attention_equals_composition():
+    q, k, v = _qkv(48, 2, 64, seed=11)
+    grid, split = (3, 4, 4), (16, 24, 24)
+    o1, l1 = oracle.attention_rope(q, k, v, grid, split)
+    o2, l2 = oracle.attention(oracle.rope3d_apply(q, grid, split),
+                              oracle.rope3d_apply(k, grid, split), v)
+    np.testing.assert_allclose(o1, o2, atol=1e-13)
+    rows = [1, 20, 47]
+    o3, l3 = oracle.attention_rope(q, k, v, grid, split, rows=rows)
+    np.testing.assert_allclose(o3, o1[rows], atol=1e-13)
+    np.testing.assert_allclose(l3, l1[:, rows], atol=1e-13)
+
+
+def test_rope_with_prefix_rows():
+    q, k, v = _qkv(6 + 48, 2, 64, seed=12)
+    grid, split = (3, 4, 4), (16, 24, 24)
+    rows = [0, 5, 6, 53]
+    o, l = oracle.attention_rope(q, k, v, grid, split, n_prefix=6, rows=rows)
+    qr = oracle.rope3d_apply(q, grid, split, n_prefix=6)
+    kr = oracle.rope3d_apply(k, grid, split, n_prefix=6)
+    o2, l2 = oracle.attention(qr, kr, v, rows=rows)
+    np.testing.assert_allclose(o, o2, atol=1e-13)
+    np.testing.assert_allclose(l, l2, atol=1e-13)
