@@ -1,0 +1,139 @@
+/*
+ * vx.h - C ABI of the MI355X (gfx950) video-DiT block hot path.
+ *
+ * Three operations, one per step of a video diffusion-transformer block as
+ * the vidax pages describe it:
+ *   vx_adaln_modulate   per-token AdaLN modulation
+ *   vx_rope3d_apply     3D rotary position embedding on Q and K
+ *   vx_flash_attn_fwd   full non-causal attention, flash style
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Tensors are caller-owned DEVICE pointers (hipMalloc or a framework
+ *   allocator), contiguous, row-major, 16-byte aligned.  The library never
+ *   allocates, frees or keeps a pointer after it returns.
+ * - Element type is given by a vx_dtype: VX_F32 (IEEE float32) or VX_BF16
+ *   (bfloat16 bits, uint16 storage).  All arithmetic is float32 inside the
+ *   kernels; bf16 results are rounded to nearest-even.
+ * - Work is enqueued on `hip_stream` (a hipStream_t; NULL = the default
+ *   stream) on the calling thread's current device.  No call synchronises.
+ * - Arguments are checked on the host before any launch.  On failure the
+ *   call returns a non-zero vx_status, launches nothing, and
+ *   vx_last_error() describes the problem.  A failed launch returns
+ *   VX_ERR_HIP.  Faults inside a kernel surface at the caller's next
+ *   synchronisation, as for any asynchronous HIP work.
+ * - Calls are re-entrant; the only global state is the per-thread error
+ *   string.
+ */
+#ifndef VX_H
+#define VX_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { VX_F32 = 0, VX_BF16 = 1 } vx_dtype;
+
+typedef enum {
+    VX_OK = 0,
+    VX_ERR_NULL = 1,        /* a required pointer is NULL                     */
+    VX_ERR_INVALID = 2,     /* sizes or parameters inconsistent or out of range */
+    VX_ERR_UNSUPPORTED = 3, /* valid, but not a shape/dtype this build serves  */
+    VX_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned                */
+    VX_ERR_HIP = 5          /* the HIP runtime reported an error at launch     */
+} vx_status;
+
+/*
+ * Position layout of a 3D RoPE (vidax paper, arXiv 2609.18077, §2 "3D RoPE,
+ * 3D VAEs, and flash attention": separate time, height and width frequency
+ * bands, one convention per model family; §3.1 "CogVideoX": joint
+ * text+video sequences whose text tokens carry no 3D position).
+ *
+ * Token order: n_prefix text tokens, then the T x H x W video grid with t
+ * outermost and w innermost; video positions are the integer grid indices
+ * (t, h, w), restarting at 0 after the prefix.  The head dimension is split
+ * into contiguous bands [t | h | w] of widths d_t, d_h, d_w (each even,
+ * d_t + d_h + d_w == head_dim).  Pair j of band a (elements 2j, 2j+1 of the
+ * band) turns by angle pos_a * theta^(-2j / d_a): (x0, x1) ->
+ * (x0 cos - x1 sin, x0 sin + x1 cos).  Text tokens are left unchanged.
+ * pairing must be 0 (adjacent pairs); other values are reserved.
+ */
+typedef struct {
+    int32_t T, H, W;       /* latent token grid                              */
+    int32_t n_prefix;      /* leading unrotated tokens; 0 if none            */
+    int32_t d_t, d_h, d_w; /* band widths                                    */
+    float theta;           /* frequency base, finite and > 0 (10000 here)    */
+    int32_t pairing;       /* 0 = adjacent pairs (2i, 2i+1)                  */
+} vx_rope3d_desc;
+
+/*
+ * Per-token AdaLN modulation (vidax paper §2 "Spatiotemporal tensor and
+ * sequence sharding" and §3.1 Table 1: Wan2.2 modulates every token with its
+ * own scale and shift after a LayerNorm; the blog post "Weight offloading:
+ * trading bandwidth for memory", section "A14B (Wan2.2)": that modulation
+ * tensor alone reaches several GB).
+ *
+ *   y[n, :] = (x[n, :] - mean_n) / sqrt(var_n + eps) * (1 + scale[n, :]) + shift[n, :]
+ *
+ * mean_n and the biased variance var_n are taken over the `hidden` values of
+ * row n; there is no learnable affine.  x, shift, scale, y: [n_rows, hidden]
+ * of type dt.  y == x (in place) is allowed; no other overlap is.
+ * Errors: VX_ERR_NULL (x, shift, scale or y NULL); VX_ERR_INVALID
+ * (n_rows < 0, hidden <= 0, eps < 0 or not finite, bad dt);
+ * VX_ERR_UNSUPPORTED (hidden not a multiple of 8 for bf16 or 4 for f32, or
+ * hidden above 8192 for bf16 or 4096 for f32: a row is held in registers);
+ * VX_ERR_ALIGN.  n_rows == 0 launches nothing.
+ */
+int vx_adaln_modulate(const void* x, const void* shift, const void* scale, void* y,
+                      int64_t n_rows, int64_t hidden, float eps, int dt, void* hip_stream);
+
+/*
+ * 3D RoPE on Q and K, in place (vidax paper §2 "3D RoPE, 3D VAEs, and flash
+ * attention").  q, k: [batch, n_tokens, heads, head_dim] of type dt; either
+ * may be NULL (that tensor is skipped) but not both; q != k.  The same
+ * angles apply to every head and batch entry.  V is never rotated.
+ * Errors: VX_ERR_NULL (q and k NULL, or rope NULL); VX_ERR_INVALID (sizes
+ * <= 0, T*H*W + n_prefix != n_tokens, grid or prefix negative, odd or
+ * mis-summed bands, theta <= 0 or not finite, pairing != 0, q == k);
+ * VX_ERR_UNSUPPORTED (head_dim not a multiple of 8, or > 256); VX_ERR_ALIGN.
+ */
+int vx_rope3d_apply(void* q, void* k, int64_t batch, int64_t n_tokens, int64_t heads,
+                    int64_t head_dim, const vx_rope3d_desc* rope, int dt, void* hip_stream);
+
+/*
+ * Full non-causal attention forward (vidax paper §1: full self-attention
+ * over every patch token of a multi-frame latent; §2 "3D RoPE, 3D VAEs, and
+ * flash attention": unmasked attention runs as flash attention, Dao et al.
+ * 2022, so the N x N score matrix is never stored).
+ *
+ *   o[b, i, h, :] = sum_j softmax_j(scale * q[b, i, h, :] . k[b, j, h, :]) v[b, j, h, :]
+ *   lse[b, h, i]  = log sum_j exp(scale * q[b, i, h, :] . k[b, j, h, :])   (natural log)
+ *
+ * q, k, v, o: [batch, n_tokens, heads, head_dim] of type dt; lse: float32
+ * [batch, heads, n_tokens] or NULL (not written).  softmax_scale <= 0 means
+ * 1/sqrt(head_dim).  If rope_q is non-NULL, Q is rotated by that 3D RoPE in
+ * registers as it is loaded (its buffer is not modified; the result equals
+ * vx_rope3d_apply on Q first); K must already be rotated.  o must not
+ * overlap q, k or v.
+ * Errors: VX_ERR_NULL (q, k, v or o NULL); VX_ERR_INVALID (sizes <= 0,
+ * softmax_scale not finite, bad rope_q as for vx_rope3d_apply, o aliasing an
+ * input); VX_ERR_UNSUPPORTED (head_dim not 64 or 128); VX_ERR_ALIGN.
+ */
+int vx_flash_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                      int64_t batch, int64_t n_tokens, int64_t heads, int64_t head_dim,
+                      float softmax_scale, const vx_rope3d_desc* rope_q, int dt,
+                      void* hip_stream);
+
+/* Message of the last failed vx_* call on this thread ("" if none). */
+const char* vx_last_error(void);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int vx_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VX_H */

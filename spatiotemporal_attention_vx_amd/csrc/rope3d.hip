@@ -1,0 +1,100 @@
+// 3D RoPE on Q and K, in place, for gfx950.
+//
+// Separate time/height/width frequency bands of the head dimension, one
+// convention per model family (vidax paper, arXiv 2609.18077, §2 "3D RoPE,
+// 3D VAEs, and flash attention"); text-prefix tokens of a joint text+video
+// sequence are not rotated (§3.1, "CogVideoX").  The position layout is the
+// one documented on vx_rope3d_desc.
+//
+// HBM-bound: each rotated row of Q and K is read and written once.  A
+// workgroup owns TPB consecutive tokens.  It first evaluates cos/sin of the
+// head_dim/2 angles of each token into LDS (angles are shared by every head
+// and by Q and K, so they cost one evaluation per token and pair), then
+// streams the 16-byte chunks of the tokens' Q and K rows, consecutive lanes
+// on consecutive chunks.
+#include "vx_device.h"
+
+namespace vx {
+
+constexpr int ROPE_TPB = 4;          // tokens per workgroup
+constexpr int ROPE_MAX_HALF = 128;   // head_dim <= 256
+
+template <bool BF16>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256)))
+void rope3d_kernel(uint4* q, uint4* k, int64_t rows, int64_t n_tokens, int heads,
+                   int head_dim, RopeArgs r) {
+    constexpr int EPC = BF16 ? 8 : 4;    // elements per 16-byte chunk
+    __shared__ f32x2_t cs[ROPE_TPB * ROPE_MAX_HALF];
+    const int half = head_dim >> 1;
+    const int64_t row0 = (int64_t)blockIdx.x * ROPE_TPB;
+
+    for (int i = threadIdx.x; i < ROPE_TPB * half; i += 256) {
+        const int tk = i / half, pair = i - tk * half;
+        const int64_t row = row0 + tk;
+        float c = 1.f, s = 0.f;
+        int pos, j, width;
+        if (row < rows && rope_pair_geometry(r, row % n_tokens, pair, &pos, &j, &width))
+            rope_cos_sin(r, pos, j, width, &c, &s);
+        cs[i] = f32x2_t{c, s};
+    }
+    __shared__ int rotate[ROPE_TPB];     // token exists and is not text
+    if (threadIdx.x < ROPE_TPB) {
+        const int64_t row = row0 + threadIdx.x;
+        rotate[threadIdx.x] = row < rows && (row % n_tokens) >= r.n_prefix;
+    }
+    __syncthreads();
+
+    const int dpr = head_dim / EPC;      // chunks per head row
+    const int cpr = heads * dpr;         // chunks per token row
+    // walk (token, tensor, chunk) with the chunk index fastest
+    int c = threadIdx.x, which = 0, tk = 0;
+    while (c >= cpr) { c -= cpr; if (++which == 2) { which = 0; ++tk; } }
+    for (; tk < ROPE_TPB;) {
+        const int64_t row = row0 + tk;
+        uint4* base = which ? k : q;
+        if (base != nullptr && rotate[tk]) {
+            uint4* p = base + row * cpr + c;
+            uint4 v = *p;
+            const f32x2_t* t = cs + tk * half + (c % dpr) * (EPC / 2);
+            if constexpr (BF16) {
+                uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    float a = bf16_lo(w[m]), b = bf16_hi(w[m]);
+                    const f32x2_t e = t[m];
+                    rope_rotate(a, b, e.x, e.y);
+                    w[m] = pack_bf16x2(a, b);
+                }
+                v = uint4{w[0], w[1], w[2], w[3]};
+            } else {
+                float f[4] = {__uint_as_float(v.x), __uint_as_float(v.y),
+                              __uint_as_float(v.z), __uint_as_float(v.w)};
+#pragma unroll
+                for (int m = 0; m < 2; ++m) {
+                    const f32x2_t e = t[m];
+                    rope_rotate(f[2 * m], f[2 * m + 1], e.x, e.y);
+                }
+                v = uint4{__float_as_uint(f[0]), __float_as_uint(f[1]),
+                          __float_as_uint(f[2]), __float_as_uint(f[3])};
+            }
+            *p = v;
+        }
+        c += 256;
+        while (c >= cpr) { c -= cpr; if (++which == 2) { which = 0; ++tk; } }
+    }
+}
+
+hipError_t launch_rope3d(void* q, void* k, int64_t batch, int64_t n_tokens, int64_t heads,
+                         int64_t head_dim, const RopeArgs& r, bool bf16, hipStream_t st) {
+    const int64_t rows = batch * n_tokens;
+    const int64_t blocks = (rows + ROPE_TPB - 1) / ROPE_TPB;
+    if (bf16)
+        hipLaunchKernelGGL(rope3d_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, st,
+                           (uint4*)q, (uint4*)k, rows, n_tokens, (int)heads, (int)head_dim, r);
+    else
+        hipLaunchKernelGGL(rope3d_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, st,
+                           (uint4*)q, (uint4*)k, rows, n_tokens, (int)heads, (int)head_dim, r);
+    return hipGetLastError();
+}
+
+}  // namespace vx

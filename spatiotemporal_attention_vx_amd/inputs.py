@@ -21,6 +21,9 @@ Recipe
 """
 from __future__ import annotations
 
+import concurrent.futures as cf
+import os
+
 import numpy as np
 
 CHUNK_ROWS = 4096
@@ -29,27 +32,50 @@ CHUNK_ROWS = 4096
 T_X, T_SHIFT, T_SCALE, T_Q, T_K, T_V, T_ROWS = range(7)
 
 
+def _chunk(seed, config_id, tensor_id, c, n_rows, width):
+    lo = c * CHUNK_ROWS
+    hi = min(lo + CHUNK_ROWS, n_rows)
+    g = np.random.Generator(np.random.PCG64(
+        np.random.SeedSequence([seed, config_id, tensor_id, c])))
+    return g.standard_normal((hi - lo, width), dtype=np.float32)
+
+
+def _workers():
+    return max(1, min(16, os.cpu_count() or 1))
+
+
 def normal_rows(seed: int, config_id: int, tensor_id: int, n_rows: int,
-                width: int, std: float = 1.0, rows=None) -> np.ndarray:
-    """float32 N(0, std) draw of shape [n_rows, width] (or [len(rows), width])."""
+                width: int, std: float = 1.0, rows=None, dtype: str = "f32") -> np.ndarray:
+    """N(0, std) draw of shape [n_rows, width] (or [len(rows), width]).
+
+    Returned in storage form for ``dtype``: float32, or bf16 bits (uint16).
+    Chunks are drawn in worker threads (numpy releases the GIL while it
+    fills an array); the result does not depend on the thread count.
+    """
+    out_dt = np.uint16 if dtype == "bf16" else np.float32
     if rows is None:
-        rows = np.arange(n_rows)
+        out = np.empty((n_rows, width), dtype=out_dt)
+
+        def fill(c):
+            a = _chunk(seed, config_id, tensor_id, c, n_rows, width)
+            if std != 1.0:
+                a *= np.float32(std)
+            out[c * CHUNK_ROWS:c * CHUNK_ROWS + a.shape[0]] = storage(a, dtype)
+
+        n_chunks = (n_rows + CHUNK_ROWS - 1) // CHUNK_ROWS
+        with cf.ThreadPoolExecutor(_workers()) as ex:
+            list(ex.map(fill, range(n_chunks)))
+        return out
     rows = np.asarray(rows, dtype=np.int64)
     out = np.empty((rows.size, width), dtype=np.float32)
-    if rows.size == 0:
-        return out
     chunk_of = rows // CHUNK_ROWS
     for c in np.unique(chunk_of):
-        lo = int(c) * CHUNK_ROWS
-        hi = min(lo + CHUNK_ROWS, n_rows)
-        g = np.random.Generator(np.random.PCG64(
-            np.random.SeedSequence([seed, config_id, tensor_id, int(c)])))
-        block = g.standard_normal((hi - lo, width), dtype=np.float32)
+        block = _chunk(seed, config_id, tensor_id, int(c), n_rows, width)
         sel = chunk_of == c
-        out[sel] = block[rows[sel] - lo]
+        out[sel] = block[rows[sel] - int(c) * CHUNK_ROWS]
     if std != 1.0:
         out *= np.float32(std)
-    return out
+    return storage(out, dtype)
 
 
 def to_bf16_bits(a: np.ndarray) -> np.ndarray:
@@ -92,8 +118,7 @@ def tensor(wl, seed: int, tensor_id: int, std: float = 1.0, rows=None) -> np.nda
     Batch entries are stacked along rows (row b*N + n is token n of batch b).
     """
     n = wl.n_tokens * wl.batch
-    return storage(normal_rows(seed, wl.config_id, tensor_id, n, wl.hidden, std, rows),
-                   wl.dtype)
+    return normal_rows(seed, wl.config_id, tensor_id, n, wl.hidden, std, rows, wl.dtype)
 
 
 def attention_inputs(wl, seed: int = 0):

@@ -1,0 +1,142 @@
+"""The C ABI: the library loads, exports what include/vx.h declares, and
+rejects bad arguments with the documented status before any launch.
+
+The argument checks run entirely on the host, so these tests pass fake
+(never dereferenced) device addresses.  They run only where no GPU is
+visible: on a GPU machine a check that wrongly passed would launch a kernel
+on those addresses, and the GPU-side tests cover the same checks with real
+tensors.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from spatiotemporal_attention_vx_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "vx.h")
+
+OK, NULL, INVALID, UNSUPPORTED, ALIGN = 0, 1, 2, 3, 4
+A = 0x10000          # fake, 16-byte aligned, never dereferenced
+MB = 1 << 20
+
+
+def declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(vx_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_three_operations():
+    names = declared()
+    for n in ("vx_adaln_modulate", "vx_rope3d_apply", "vx_flash_attn_fwd", "vx_last_error",
+              "vx_version"):
+        assert n in names
+    assert set(names) == set(binding.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = binding.load()
+    for n in declared():
+        assert hasattr(lib, n), n
+    assert lib.vx_version() >= 100
+
+
+def test_rope_desc_layout_matches_header():
+    # nine 4-byte fields, no padding
+    assert ctypes.sizeof(binding.RopeDesc) == 36
+
+
+def _gpu_visible():
+    import torch
+    return torch.cuda.is_available()
+
+
+host_only = pytest.mark.skipif(_gpu_visible(), reason="fake-address checks run only without a GPU")
+
+
+def _rope(**kw):
+    d = dict(T=2, H=3, W=4, n_prefix=0, d_t=16, d_h=24, d_w=24, theta=10000.0, pairing=0)
+    d.update(kw)
+    return binding.RopeDesc(**d)
+
+
+@host_only
+@pytest.mark.parametrize("args,code", [
+    ((None, A, A, A + 3 * MB, 4, 64, 1e-6, 1), NULL),
+    ((A, A + MB, A + 2 * MB, A + 3 * MB, -1, 64, 1e-6, 1), INVALID),
+    ((A, A + MB, A + 2 * MB, A + 3 * MB, 4, 0, 1e-6, 1), INVALID),
+    ((A, A + MB, A + 2 * MB, A + 3 * MB, 4, 64, -1.0, 1), INVALID),
+    ((A, A + MB, A + 2 * MB, A + 3 * MB, 4, 64, float("nan"), 1), INVALID),
+    ((A, A + MB, A + 2 * MB, A + 3 * MB, 4, 64, 1e-6, 7), INVALID),
+    ((A, A + MB, A + 2 * MB, A + 3 * MB, 4, 60, 1e-6, 1), UNSUPPORTED),
+    ((A, A + MB, A + 2 * MB, A + 3 * MB, 4, 8200, 1e-6, 1), UNSUPPORTED),
+    ((A, A + MB, A + 2 * MB, A + 3 * MB, 4, 4100, 1e-6, 0), UNSUPPORTED),
+    ((A + 2, A + MB, A + 2 * MB, A + 3 * MB, 4, 64, 1e-6, 1), ALIGN),
+    ((A, A + MB, A + 2 * MB, A + 64, 4, 64, 1e-6, 1), INVALID),       # y overlaps x
+    ((A, A + MB, A + 2 * MB, A + MB, 4, 64, 1e-6, 1), INVALID),       # y == shift
+    ((A, A + 64, A + 2 * MB, A, 4, 64, 1e-6, 1), INVALID),            # in place, shift overlaps
+])
+def test_adaln_rejects(args, code):
+    lib = binding.load()
+    assert lib.vx_adaln_modulate(*args, None) == code
+    assert lib.vx_last_error().decode().startswith("vx_adaln_modulate")
+
+
+@host_only
+def test_adaln_zero_rows_is_a_no_op():
+    lib = binding.load()
+    assert lib.vx_adaln_modulate(A, A + MB, A + 2 * MB, A + 3 * MB, 0, 64, 1e-6, 1, None) == OK
+    assert lib.vx_last_error() == b""
+
+
+@host_only
+@pytest.mark.parametrize("q,k,n,d,rope,code", [
+    (None, None, 24, 64, _rope(), NULL),
+    (A, A + MB, 24, 64, None, NULL),
+    (A, A, 24, 64, _rope(), INVALID),                          # q == k
+    (A, A + 64, 24, 64, _rope(), INVALID),                     # overlap
+    (A, A + MB, 25, 64, _rope(), INVALID),                     # grid != tokens
+    (A, A + MB, 24, 64, _rope(d_t=15, d_h=25), INVALID),       # odd band
+    (A, A + MB, 24, 64, _rope(d_t=18), INVALID),               # bands sum != d
+    (A, A + MB, 24, 64, _rope(theta=0.0), INVALID),
+    (A, A + MB, 24, 64, _rope(theta=float("inf")), INVALID),
+    (A, A + MB, 24, 64, _rope(pairing=1), INVALID),
+    (A, A + MB, 24, 64, _rope(T=-1), INVALID),
+    (A, A + MB, 24, 60, _rope(d_t=12), UNSUPPORTED),
+    (A, A + MB, 24, 264, _rope(d_t=216), UNSUPPORTED),
+    (A + 8, A + MB, 24, 64, _rope(), ALIGN),
+])
+def test_rope_rejects(q, k, n, d, rope, code):
+    lib = binding.load()
+    r = ctypes.byref(rope) if rope is not None else None
+    assert lib.vx_rope3d_apply(q, k, 1, n, 2, d, r, 1, None) == code
+
+
+@host_only
+@pytest.mark.parametrize("ptrs,n,d,scale,rope,dt,code", [
+    ((None, A + MB, A + 2 * MB, A + 3 * MB, None), 24, 64, 0.0, None, 1, NULL),
+    ((A, A + MB, A + 2 * MB, A + 3 * MB, None), 0, 64, 0.0, None, 1, INVALID),
+    ((A, A + MB, A + 2 * MB, A + 3 * MB, None), 24, 64, float("inf"), None, 1, INVALID),
+    ((A, A + MB, A + 2 * MB, A + 3 * MB, None), 24, 96, 0.0, None, 1, UNSUPPORTED),
+    ((A, A + MB, A + 2 * MB, A + 3 * MB, None), 24, 256, 0.0, None, 1, UNSUPPORTED),
+    ((A, A + MB, A + 2 * MB, A + 3 * MB, None), 24, 64, 0.0, None, 2, INVALID),
+    ((A, A + MB, A + 2 * MB, A + 3 * MB, None), 25, 64, 0.0, _rope(), 1, INVALID),
+    ((A, A + MB, A + 2 * MB, A + 3 * MB + 4, None), 24, 64, 0.0, None, 1, ALIGN),
+    ((A, A + MB, A + 2 * MB, A + 3 * MB, A + 4 * MB + 2), 24, 64, 0.0, None, 1, ALIGN),
+    ((A, A + MB, A + 2 * MB, A + 32, None), 24, 64, 0.0, None, 1, INVALID),   # o overlaps q
+    ((A, A + MB, A + 2 * MB, A + 3 * MB, A + 3 * MB), 24, 64, 0.0, None, 1, INVALID),
+])
+def test_attention_rejects(ptrs, n, d, scale, rope, dt, code):
+    lib = binding.load()
+    r = ctypes.byref(rope) if rope is not None else None
+    assert lib.vx_flash_attn_fwd(*ptrs, 1, n, 2, d, scale, r, dt, None) == code
+    assert lib.vx_last_error().decode().startswith("vx_flash_attn_fwd")
+
+
+def test_binding_refuses_mismatched_tensors():
+    import torch
+    x = torch.zeros(4, 64)
+    with pytest.raises(ValueError):
+        binding.adaln_modulate(x, x, x, x)          # not on a GPU

@@ -1,0 +1,135 @@
+"""GPU parity of vx_flash_attn_fwd (and the RoPE + attention path) against
+the fp64 oracle."""
+import numpy as np
+import pytest
+
+import oracle
+from _helpers import bits, check, dev, host, say
+from spatiotemporal_attention_vx_amd import binding, configs, inputs
+
+pytestmark = pytest.mark.gpu
+
+# The bf16 LSE: scores are fp32 sums of exact bf16 products, so the error is
+# a few fp32 ulps of |s| times the log-sum-exp's sensitivity (<= 1).
+LSE_TOL = {"f32": 1e-5, "bf16": 1e-4}
+
+
+def _rand(shape, dtype, seed):
+    g = np.random.default_rng(seed)
+    return inputs.storage(g.standard_normal(shape).astype(np.float32), dtype)
+
+
+def _attn(q, k, v, with_lse=True, scale=0.0, rope_q=None):
+    import torch
+    tq, tk, tv = dev(q), dev(k), dev(v)
+    o = torch.full_like(tq, float("nan"))
+    b, n, h, _ = tq.shape
+    lse = torch.full((b, h, n), float("nan"), device="cuda") if with_lse else None
+    binding.flash_attn_fwd(tq, tk, tv, o, lse, scale, rope_q)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("n,heads,d,batch", [
+    (1, 1, 64, 1), (2, 2, 128, 1), (63, 1, 64, 1), (64, 3, 128, 1), (65, 2, 64, 2),
+    (127, 1, 128, 1), (128, 2, 64, 1), (129, 3, 128, 1), (200, 2, 64, 2), (1000, 2, 128, 1),
+    (4097, 1, 64, 1),
+])
+def test_ragged(gpu_lib, dtype, n, heads, d, batch):
+    say(f"attn ragged {dtype} n={n} heads={heads} d={d} batch={batch}")
+    shape = (batch, n, heads, d)
+    q, k, v = (_rand(shape, dtype, n * 7 + i) for i in range(3))
+    o, lse = _attn(q, k, v)
+    og, lg = host(o), lse.cpu().numpy()
+    for b in range(batch):
+        ref, rl = oracle.attention(inputs.values(q[b]), inputs.values(k[b]), inputs.values(v[b]))
+        check(og[b], ref, dtype, f"o[{b}]")
+        assert np.abs(lg[b] - rl).max() <= LSE_TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_explicit_scale(gpu_lib, dtype):
+    say(f"attn explicit scale {dtype}")
+    shape = (1, 300, 2, 128)
+    q, k, v = (_rand(shape, dtype, 50 + i) for i in range(3))
+    o, lse = _attn(q, k, v, scale=0.05)
+    ref, rl = oracle.attention(inputs.values(q[0]), inputs.values(k[0]), inputs.values(v[0]),
+                               scale=0.05)
+    check(host(o)[0], ref, dtype, "o")
+    assert np.abs(lse.cpu().numpy()[0] - rl).max() <= LSE_TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("d", [64, 128])
+def test_single_token_returns_v_exactly(gpu_lib, dtype, d):
+    say(f"attn N=1 {dtype} d={d}")
+    q, k, v = (_rand((2, 1, 3, d), dtype, 90 + i) for i in range(3))
+    o, lse = _attn(q, k, v)
+    np.testing.assert_array_equal(host(o), inputs.values(v))
+    s = np.einsum("bnhd,bnhd->bhn", inputs.values(q).astype(np.float64),
+                  inputs.values(k).astype(np.float64)) / np.sqrt(d)
+    assert np.abs(lse.cpu().numpy() - s).max() <= LSE_TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_equal_keys_give_mean_of_v(gpu_lib, dtype):
+    say(f"attn equal keys {dtype}")
+    n = 333
+    q, k, v = (_rand((1, n, 2, 64), dtype, 120 + i) for i in range(3))
+    k[:] = k[:, :1]
+    o, _ = _attn(q, k, v, with_lse=False)
+    mean = inputs.values(v).astype(np.float64).mean(axis=1, keepdims=True)
+    check(host(o), np.broadcast_to(mean, o.shape), dtype, "o")
+
+
+@pytest.mark.parametrize("name", ["tiny", "small"])
+def test_fused_rope_q_matches_separate(gpu_lib, name):
+    import torch
+    wl = configs.WORKLOADS[name]
+    say(f"attn fused rope_q {name}")
+    q, k, v = inputs.attention_inputs(wl)
+    desc = binding.RopeDesc.of(wl.grid, wl.split, wl.theta, wl.n_prefix)
+    tq, tk, tv = dev(q), dev(k), dev(v)
+    binding.rope3d_apply(tq, tk, desc)
+    o1 = torch.empty_like(tq)
+    binding.flash_attn_fwd(tq, tk, tv, o1)
+    tq0 = dev(q)
+    o2 = torch.empty_like(tq)
+    binding.flash_attn_fwd(tq0, tk, tv, o2, rope_q=desc)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(bits(o2), bits(o1))
+    np.testing.assert_array_equal(bits(tq0), q.view(np.int16 if q.dtype == np.uint16 else np.int32))
+
+
+@pytest.mark.timeout(1200)
+@pytest.mark.parametrize("name", list(configs.WORKLOADS))
+@pytest.mark.parametrize("fused", [False, True])
+def test_workload_rope_then_attention(gpu_lib, name, fused):
+    """The whole hot path at each workload's real size; the oracle checks all
+    rows on the small workloads and 256 seeded rows (all heads, all keys) on
+    the large ones."""
+    import torch
+    wl = configs.WORKLOADS[name]
+    if fused and name not in ("small", "large"):
+        pytest.skip("fused Q rotation is covered on small and large")
+    say(f"attn workload {name} fused={fused}: N={wl.n_tokens} H={wl.heads} d={wl.head_dim}")
+    q, k, v = inputs.attention_inputs(wl)
+    desc = binding.RopeDesc.of(wl.grid, wl.split, wl.theta, wl.n_prefix)
+    tq, tk, tv = dev(q), dev(k), dev(v)
+    binding.rope3d_apply(None if fused else tq, tk, desc)
+    o = torch.empty_like(tq)
+    lse = torch.empty((1, wl.heads, wl.n_tokens), device="cuda")
+    binding.flash_attn_fwd(tq, tk, tv, o, lse, rope_q=desc if fused else None)
+    torch.cuda.synchronize()
+    del tq, tk, tv
+    rows = inputs.sample_rows(wl)
+    og = host(o)[0, rows]
+    lg = lse.cpu().numpy()[0][:, rows]
+    del o, lse
+    ref, rl = oracle.attention_rope(inputs.values(q[0]), inputs.values(k[0]), inputs.values(v[0]),
+                                    wl.grid, wl.split, wl.theta, wl.n_prefix, rows=rows)
+    check(og, ref, wl.dtype, f"attn {name}")
+    zero_rel = 1.0
+    say(f"  (an all-zero output would have rel L2 {zero_rel:.1f})")
+    assert np.abs(lg - rl).max() <= LSE_TOL[wl.dtype]

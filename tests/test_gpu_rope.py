@@ -1,0 +1,90 @@
+"""GPU parity of vx_rope3d_apply against the fp64 oracle."""
+import numpy as np
+import pytest
+
+import oracle
+from _helpers import bits, check, dev, host, say
+from spatiotemporal_attention_vx_amd import binding, configs, inputs
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", list(configs.WORKLOADS))
+def test_workload(gpu_lib, name):
+    import torch
+    wl = configs.WORKLOADS[name]
+    say(f"rope workload {name}: N={wl.n_tokens} H={wl.heads} d={wl.head_dim} {wl.dtype}")
+    q, k, _ = inputs.attention_inputs(wl)
+    tq, tk = dev(q), dev(k)
+    desc = binding.RopeDesc.of(wl.grid, wl.split, wl.theta, wl.n_prefix)
+    binding.rope3d_apply(tq, tk, desc)
+    torch.cuda.synchronize()
+    rows = inputs.sample_rows(wl, count=2048 if wl.oracle_rows else 0)
+    for src, t, nm in ((q, tq, "q"), (k, tk, "k")):
+        got = host(t)[0, rows]
+        x = inputs.values(src[0, rows]).astype(np.float64)
+        ref = oracle.rope3d_apply(x, wl.grid, wl.split, wl.theta, wl.n_prefix, tokens=rows)
+        check(got, ref, wl.dtype, f"rope {name} {nm}")
+    if wl.n_prefix:
+        # text tokens are not touched at all
+        np.testing.assert_array_equal(bits(tq)[0, :wl.n_prefix],
+                                      q[0, :wl.n_prefix].view(np.int16))
+
+
+@pytest.mark.parametrize("dtype,grid,prefix,heads,d,batch,split", [
+    ("f32", (1, 1, 1), 0, 1, 64, 1, (16, 24, 24)),
+    ("f32", (2, 3, 5), 7, 3, 128, 2, (44, 42, 42)),
+    ("bf16", (2, 3, 5), 7, 3, 128, 2, (44, 42, 42)),
+    ("bf16", (3, 1, 4), 0, 5, 64, 1, (16, 24, 24)),
+    ("bf16", (2, 2, 2), 1, 2, 8, 1, (2, 2, 4)),
+    ("bf16", (2, 4, 3), 0, 1, 256, 3, (64, 96, 96)),
+    ("bf16", (5, 2, 3), 3, 2, 96, 1, (0, 48, 48)),
+])
+def test_ragged(gpu_lib, dtype, grid, prefix, heads, d, batch, split):
+    import torch
+    n = prefix + grid[0] * grid[1] * grid[2]
+    say(f"rope ragged {dtype} grid={grid} prefix={prefix} heads={heads} d={d} batch={batch}")
+    g = np.random.default_rng(n * 31 + d)
+    q = inputs.storage(g.standard_normal((batch, n, heads, d)).astype(np.float32), dtype)
+    k = inputs.storage(g.standard_normal((batch, n, heads, d)).astype(np.float32), dtype)
+    tq, tk = dev(q), dev(k)
+    binding.rope3d_apply(tq, tk, binding.RopeDesc.of(grid, split, 10000.0, prefix))
+    torch.cuda.synchronize()
+    for src, t, nm in ((q, tq, "q"), (k, tk, "k")):
+        got = host(t)
+        for b in range(batch):
+            ref = oracle.rope3d_apply(inputs.values(src[b]).astype(np.float64), grid, split,
+                                      10000.0, prefix)
+            check(got[b], ref, dtype, f"rope ragged {nm}[{b}]")
+
+
+def test_single_tensor_calls_match_pair_call(gpu_lib):
+    import torch
+    say("rope q-only / k-only")
+    wl = configs.WORKLOADS["small"]
+    q, k, _ = inputs.attention_inputs(wl)
+    desc = binding.RopeDesc.of(wl.grid, wl.split, wl.theta, wl.n_prefix)
+    tq, tk = dev(q), dev(k)
+    binding.rope3d_apply(tq, tk, desc)
+    tq1, tk1 = dev(q), dev(k)
+    binding.rope3d_apply(tq1, None, desc)
+    binding.rope3d_apply(None, tk1, desc)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(bits(tq1), bits(tq))
+    np.testing.assert_array_equal(bits(tk1), bits(tk))
+
+
+def test_f32_norm_preserved(gpu_lib):
+    import torch
+    say("rope f32 norm")
+    wl = configs.WORKLOADS["tiny"]
+    q, k, _ = inputs.attention_inputs(wl)
+    tq = dev(q)
+    binding.rope3d_apply(tq, None, binding.RopeDesc.of(wl.grid, wl.split, wl.theta))
+    torch.cuda.synchronize()
+    got = host(tq).astype(np.float64)
+    x = inputs.values(q).astype(np.float64)
+    n0 = x[..., 0::2] ** 2 + x[..., 1::2] ** 2
+    n1 = got[..., 0::2] ** 2 + got[..., 1::2] ** 2
+    np.testing.assert_allclose(n1, n0, rtol=2e-6, atol=1e-6)
