@@ -296,6 +296,10 @@ constexpr int FA32_BC = 32;
 template <int D>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256)))
 void fa_fwd_f32_kernel(FaArgs a) {
+    // Every fused multiply-add below is spelled out; implicit contraction is
+    // off so each score is rounded once and the same value feeds the running
+    // max and the exponent (a lone key then weighs exactly 1).
+#pragma clang fp contract(off)
     constexpr int TPQ = D / 32;        // lanes per query, 32 elements each
     constexpr int QPB = 256 / TPQ;     // queries per workgroup
     __shared__ __attribute__((aligned(16))) float ks[FA32_BC * D];

@@ -12,6 +12,12 @@ pytestmark = pytest.mark.gpu
 # The bf16 LSE: scores are fp32 sums of exact bf16 products, so the error is
 # a few fp32 ulps of |s| times the log-sum-exp's sensitivity (<= 1).
 LSE_TOL = {"f32": 1e-5, "bf16": 1e-4}
+# After RoPE the rotated Q and K are stored in bf16 (relative rounding up to
+# 2^-9 per element) while the oracle rotates in fp64.  A score then moves by
+# about scale * sqrt(2 d) * 2^-9 / sqrt(3) ~ 1.6e-3 (RMS, d = 128, unit
+# inputs); the LSE, a softmax-weighted mean of score moves, stays within a
+# few of those.
+LSE_TOL_ROPE = {"f32": 1e-5, "bf16": 1e-2}
 
 
 def _rand(shape, dtype, seed):
@@ -130,6 +136,8 @@ def test_workload_rope_then_attention(gpu_lib, name, fused):
     ref, rl = oracle.attention_rope(inputs.values(q[0]), inputs.values(k[0]), inputs.values(v[0]),
                                     wl.grid, wl.split, wl.theta, wl.n_prefix, rows=rows)
     check(og, ref, wl.dtype, f"attn {name}")
-    zero_rel = 1.0
-    say(f"  (an all-zero output would have rel L2 {zero_rel:.1f})")
-    assert np.abs(lg - rl).max() <= LSE_TOL[wl.dtype]
+    say(f"  output rms {float(np.sqrt(np.mean(ref ** 2))):.3e} "
+        f"(an all-zero output has rel L2 1.0)")
+    lse_err = float(np.abs(lg - rl).max())
+    say(f"  lse max abs {lse_err:.3e}")
+    assert lse_err <= LSE_TOL_ROPE[wl.dtype]
