@@ -1,0 +1,211 @@
+#!/usr/bin/env python3
+"""Benchmark of the video-DiT block hot path on one MI355X.
+
+One step = the whole hot path over one batch of synthetic input at the
+75,600-token workload (21x45x80 latent grid, 40 heads x 128, bf16, batch 1):
+
+  1. per-token AdaLN modulation of x [75600, 5120]   (vx_adaln_modulate)
+  2. 3D RoPE on K (and on Q unless it is fused)      (vx_rope3d_apply)
+  3. full non-causal flash attention                 (vx_flash_attn_fwd)
+
+Inputs are generated on the host, copied to HBM once, and stay resident;
+the timed region holds only the three launches per step.  The reported
+value is attention TFLOP/s (4 N^2 d H per step) over the whole step time.
+The dominant kernel (attention) is also timed alone with HIP events on the
+stream it is launched on, and compared with the bf16 dense MFMA peak.
+
+The CPU baseline times the fp64 oracle on a bounded sample of the same
+workload (a few query rows, every head, every key) on the host cores.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+METRIC = "flash-attn TFLOP/s + % bf16 MFMA peak at 75,600 tokens, 40 heads × d128"
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--workload", default="large")
+    p.add_argument("--rope", choices=["fused", "separate"], default="fused",
+                   help="fused: K rotated by vx_rope3d_apply, Q inside the attention load")
+    p.add_argument("--cpu-rows", type=int, default=64,
+                   help="query rows of the oracle CPU baseline (0 = skip it)")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="also run a plain 1 GiB elementwise copy (HBM counter calibration)")
+    return p.parse_args()
+
+
+def cpu_baseline(wl, q, k, v, rows_count):
+    """The oracle, as it stands, on `rows_count` query rows x all heads x all keys."""
+    import numpy as np
+    import oracle
+    from spatiotemporal_attention_vx_amd import inputs
+    try:
+        import threadpoolctl
+        threads = max(i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()) or 1
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    rows = inputs.sample_rows(wl, count=rows_count)
+    qv, kv, vv = inputs.values(q[0]), inputs.values(k[0]), inputs.values(v[0])
+    t0 = time.perf_counter()
+    oracle.attention_rope(qv, kv, vv, wl.grid, wl.split, wl.theta, wl.n_prefix, rows=rows)
+    dt = time.perf_counter() - t0
+    flops = 4.0 * rows.size * wl.n_tokens * wl.head_dim * wl.heads
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": (f"fp64 oracle, RoPE on Q and K then attention, {rows.size} seeded query "
+                       f"rows x {wl.heads} heads x all {wl.n_tokens} keys of the same workload; "
+                       f"{dt:.1f} s wall, {flops / 1e9:.1f} GFLOP"),
+            "seconds": dt}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
+              f"(the path would shard heads across GPUs; no multi-GPU run is built)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from spatiotemporal_attention_vx_amd import binding, configs, inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    binding.load()
+    wl = configs.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    props = torch.cuda.get_device_properties(dev)
+
+    # ---- inputs: host generation (seeded), one copy to HBM
+    t0 = time.perf_counter()
+    q, k, v = inputs.attention_inputs(wl)
+    x, sh, sc = inputs.adaln_inputs(wl)
+
+    def up(a):
+        return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+
+    tq, tk, tv = up(q), up(k), up(v)
+    tx, tsh, tsc = up(x), up(sh), up(sc)
+    ty = torch.empty_like(tx)
+    to = torch.empty_like(tq)
+    gen_s = time.perf_counter() - t0
+    desc = binding.RopeDesc.of(wl.grid, wl.split, wl.theta, wl.n_prefix)
+    fused = args.rope == "fused"
+    stream = torch.cuda.current_stream()
+
+    ev = {name: [] for name in ("adaln", "rope", "attn")}
+
+    def step(record):
+        marks = [torch.cuda.Event(enable_timing=True) for _ in range(4)] if record else None
+        if record:
+            marks[0].record(stream)
+        binding.adaln_modulate(tx, tsh, tsc, ty, wl.eps, stream=stream)
+        if record:
+            marks[1].record(stream)
+        binding.rope3d_apply(None if fused else tq, tk, desc, stream=stream)
+        if record:
+            marks[2].record(stream)
+        binding.flash_attn_fwd(tq, tk, tv, to, None, 0.0, desc if fused else None, stream=stream)
+        if record:
+            marks[3].record(stream)
+            ev["adaln"].append((marks[0], marks[1]))
+            ev["rope"].append((marks[1], marks[2]))
+            ev["attn"].append((marks[2], marks[3]))
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 29, dtype=torch.bfloat16, device=dev).normal_()
+        dst = torch.empty_like(src)
+        torch.neg(src, out=dst)          # 1 GiB read + 1 GiB written, one elementwise kernel
+        torch.cuda.synchronize()
+        del src, dst
+
+    ms = {kname: float(np.mean([a.elapsed_time(b) for a, b in pairs]))
+          for kname, pairs in ev.items()}
+    ms_step = wall * 1e3 / args.steps
+    flops = wl.attn_flops()
+    value = flops / (ms_step * 1e-3) / 1e12
+    attn_tflops = flops / (ms["attn"] * 1e-3) / 1e12
+    rope_bytes = wl.rope_bytes() / (1 if not fused else 2)     # fused: K only
+    kernels = {
+        "attn_ms": round(ms["attn"], 4),
+        "attn_tflops": round(attn_tflops, 2),
+        "attn_exps": float(wl.n_tokens) ** 2 * wl.heads,
+        "adaln_ms": round(ms["adaln"], 4),
+        "adaln_gbs": round(wl.adaln_bytes() / (ms["adaln"] * 1e-3) / 1e9, 1),
+        "adaln_hbm_frac": round(wl.adaln_bytes() / (ms["adaln"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+        "rope_ms": round(ms["rope"], 4),
+        "rope_tensors": "K" if fused else "Q,K",
+        "rope_gbs": round(rope_bytes / (ms["rope"] * 1e-3) / 1e9, 1),
+        "rope_hbm_frac": round(rope_bytes / (ms["rope"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+    }
+    record = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": (f"{wl.name}: {wl.grid[0]}x{wl.grid[1]}x{wl.grid[2]} latent grid"
+                         + (f" + {wl.n_prefix} text tokens" if wl.n_prefix else "")
+                         + f", {wl.n_tokens} tokens, {wl.heads} heads x {wl.head_dim}, "
+                         f"{wl.dtype}, batch {wl.batch}"),
+            "tokens": wl.n_tokens, "heads": wl.heads, "head_dim": wl.head_dim,
+            "batch": wl.batch, "rope": args.rope,
+            "step": "adaln [N, H*d] + rope3d + flash attention fwd",
+        },
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(attn_tflops, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
+            "traffic": None,
+            "kernel": "fa_fwd_bf16_kernel<128>",
+        },
+        "kernels": kernels,
+        "device": {"name": props.name, "cus": props.multi_processor_count,
+                   "gcn_arch": getattr(props, "gcnArchName", "")},
+        "input_setup_s": round(gen_s, 2),
+    }
+    if args.cpu_rows > 0:
+        record["cpu_baseline"] = cpu_baseline(wl, q, k, v, args.cpu_rows)
+    print(json.dumps(record), flush=True)
+
+
+if __name__ == "__main__":
+    main()
