@@ -80,7 +80,32 @@ __device__ __forceinline__ int swap_bits23(int p) {
     return (p & ~12) | ((p & 4) << 1) | ((p & 8) >> 1);
 }
 
-__device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
+// {x[l % 32], x[l % 32 + 32]} in some order, for every lane l, through
+// v_permlane32_swap (no LDS round trip); max and sum are symmetric in them.
+__device__ __forceinline__ float half_max(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                    false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float half_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                    false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// 2^x with the bare v_exp_f32 (results below 2^-126 may flush to zero,
+// which only drops weights already negligible against the row maximum).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Buffer resource over [base, base + bytes): loads past the end return 0.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, int64_t bytes) {
+    const int32_t n = bytes > 0x7fffffff ? 0x7fffffff : (bytes < 0 ? 0 : (int32_t)bytes);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, 0x00020000);
+}
+
+// A lazily rescaled running maximum may trail the true one by up to this
+// many powers of two before the accumulator is rescaled (weights <= 2^8).
+constexpr float FA_LAZY_LOG2 = 8.0f;
 
 template <int D>
 __device__ __forceinline__ void load_q_fragment(const FaArgs& a, const uint16_t* qb, int64_t qi,
@@ -134,24 +159,34 @@ void fa_fwd_bf16_kernel(FaArgs a) {
     load_q_fragment<D>(a, qb, qi, g, qf);
 
     // ---- tile staging: global -> registers -> LDS
-    uint4 kreg[S::KCH];
+    // Each thread's byte offsets inside a tile are fixed; the tile start
+    // and the sequence end live in a per-tile scalar buffer resource, so
+    // keys past the end read as zero without any per-lane bounds test.
+    u32x4_t kreg[S::KCH];
     uint2 vreg[S::KPT];
     const int vdq = tid % S::DQ, vkg = tid / S::DQ;
+    const int64_t row_bytes = a.row_stride * 2;
+    uint32_t koff[S::KCH], voff[S::KPT];
+#pragma unroll
+    for (int i = 0; i < S::KCH; ++i) {
+        const int c = tid + 256 * i;
+        koff[i] = (uint32_t)((c / (D / 8)) * row_bytes + (c % (D / 8)) * 16);
+    }
+#pragma unroll
+    for (int s = 0; s < S::KPT; ++s)
+        voff[s] = (uint32_t)(swap_bits23(vkg * S::KPT + s) * row_bytes + vdq * 8);
 
     auto load_tile = [&](int64_t kv0) {
+        const int64_t left = (n - kv0) * row_bytes;
+        const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(kb + kv0 * a.row_stride, left);
+        const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(vb + kv0 * a.row_stride, left);
 #pragma unroll
-        for (int i = 0; i < S::KCH; ++i) {
-            const int c = tid + 256 * i;
-            const int key = c / (D / 8), col = c % (D / 8);
-            const int64_t kk = kv0 + key;
-            kreg[i] = kk < n ? *(const uint4*)(kb + kk * a.row_stride + col * 8)
-                             : uint4{0u, 0u, 0u, 0u};
-        }
+        for (int i = 0; i < S::KCH; ++i)
+            kreg[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, koff[i], 0, 0);
 #pragma unroll
         for (int s = 0; s < S::KPT; ++s) {
-            const int64_t kk = kv0 + swap_bits23(vkg * S::KPT + s);
-            vreg[s] = kk < n ? *(const uint2*)(vb + kk * a.row_stride + vdq * 4)
-                             : uint2{0u, 0u};
+            const auto w = __builtin_amdgcn_raw_buffer_load_b64(rv, voff[s], 0, 0);
+            vreg[s] = uint2{w[0], w[1]};
         }
     };
     auto store_tile = [&](int buf) {
@@ -161,7 +196,7 @@ void fa_fwd_bf16_kernel(FaArgs a) {
         for (int i = 0; i < S::KCH; ++i) {
             const int c = tid + 256 * i;
             const int key = c / (D / 8), col = c % (D / 8);
-            *(uint4*)(ks + key * S::KROW + col * 8) = kreg[i];
+            *(u32x4_t*)(ks + key * S::KROW + col * 8) = kreg[i];
         }
         // transpose: element j of each of the KPT keys -> one V^T row segment
 #pragma unroll
@@ -226,24 +261,29 @@ void fa_fwd_bf16_kernel(FaArgs a) {
         for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
             for (int i = 0; i < 16; ++i) mx = fmaxf(mx, st[kb2][i]);
-        mx = fmaxf(mx, xor32(mx));
-        const float m_new = fmaxf(m_run, mx);
-        const float alpha = exp2f((m_run - m_new) * a.scale_log2);
-        const float mb = m_new * a.scale_log2;
-        m_run = m_new;
+        mx = half_max(mx);
+        // Rescale only when some row's maximum outgrew the reference by more
+        // than 2^FA_LAZY_LOG2 (always on the first tile, where m_run = -inf).
+        if (__builtin_amdgcn_ballot_w64((mx - m_run) * a.scale_log2 > FA_LAZY_LOG2) != 0) {
+            const float m_new = fmaxf(m_run, mx);
+            const float alpha = fast_exp2((m_run - m_new) * a.scale_log2);
+            m_run = m_new;
+            l_run *= alpha;
+#pragma unroll
+            for (int i = 0; i < D / 32; ++i) acc[i] *= alpha;
+        }
+        const float mb = m_run * a.scale_log2;
 
         float psum = 0.f;
 #pragma unroll
         for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                const float p = exp2f(__builtin_fmaf(st[kb2][i], a.scale_log2, -mb));
+                const float p = fast_exp2(__builtin_fmaf(st[kb2][i], a.scale_log2, -mb));
                 st[kb2][i] = p;
                 psum += p;
             }
-        l_run = __builtin_fmaf(l_run, alpha, psum);
-#pragma unroll
-        for (int i = 0; i < D / 32; ++i) acc[i] *= alpha;
+        l_run += psum;
 
         // P^T operand: 16 keys per MFMA, taken from accumulator slots 0-7 / 8-15
         bf16x8_t pb[FA_BC / 16];
@@ -270,7 +310,7 @@ void fa_fwd_bf16_kernel(FaArgs a) {
     }
 
     // epilogue: combine the two halves' row sums, normalise, store
-    const float l_tot = l_run + xor32(l_run);
+    const float l_tot = half_sum(l_run);
     const float inv = 1.0f / l_tot;
     if (qi < n) {
         uint16_t* ob = a.o + off + qi * a.row_stride;
