@@ -43,7 +43,7 @@ def parse():
     p.add_argument("--workload", default="large")
     p.add_argument("--rope", choices=["fused", "separate"], default="fused",
                    help="fused: K rotated by vx_rope3d_apply, Q inside the attention load")
-    p.add_argument("--cpu-rows", type=int, default=64,
+    p.add_argument("--cpu-rows", type=int, default=192,
                    help="query rows of the oracle CPU baseline (0 = skip it)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run a plain 1 GiB elementwise copy (HBM counter calibration)")
