@@ -8,28 +8,46 @@
 // attention, Dao et al. 2022: an online softmax over key tiles, so the
 // N x N score matrix never exists).
 //
-// bf16 path (the hot one), per workgroup of 4 waves and 128 query rows:
-//   * Each wave owns 32 query rows.  Scores are formed transposed,
-//     S^T (32 keys x 32 queries) = K_tile . Q^T, with
-//     v_mfma_f32_32x32x16_bf16: K rows come from LDS as the A operand, the
-//     wave's Q^T fragment stays in VGPRs as the B operand.  In the
+// bf16 path (the hot one).  A workgroup of WAVES waves owns 32 * WAVES
+// query rows of one (batch, head); each wave owns 32 rows.
+//   * Scores are formed transposed, S^T (32 keys x 32 queries) = K_tile Q^T,
+//     with v_mfma_f32_32x32x16_bf16: K rows come from LDS as the A operand,
+//     the wave's Q^T fragment stays in VGPRs as the B operand.  In the
 //     accumulator, lane l holds query l % 32 and 16 of the 32 keys, so the
-//     softmax row statistics are per lane, plus one exchange with lane l^32.
+//     row statistics are per lane plus one exchange with lane l ^ 32.
+//   * Everything is in base-2 units: Q is multiplied by scale * log2(e) as
+//     it is loaded, and the running row maximum m enters each score through
+//     the MFMA's C operand (a register block holding -m), so the MFMA hands
+//     out u - m directly and the softmax weight is a bare v_exp_f32.
+//   * m is raised lazily: only when some row's maximum exceeds it by more
+//     than 2^8 in weight are the accumulator, the row sums and -m updated.
+//     Weights are therefore <= 2^8, and the final division uses the m that
+//     was actually subtracted, so the result is exact up to rounding.
 //   * P^T is rounded to bf16 in registers and is directly the B operand of
-//     O^T (d x 32 queries) += V^T . P^T.  The k index of that product runs
-//     over keys in the order the S^T accumulator hands them out; V^T is
-//     stored in LDS with the same key order, so no shuffle is needed.
-//   * K (row-major) and V^T (transposed while it is written to LDS) are
-//     double-buffered: tile t+1 is fetched into registers while tile t is
-//     computed, and written to the other LDS buffer before the barrier.
-//   * Key tiles past the sequence end are zero-filled and their scores set
-//     to -inf; query rows past the end are computed on zeros and not stored.
+//     O^T (d x 32 queries) += V^T P^T; the k index of that product runs
+//     over keys in the order the S^T accumulator hands them out, and V^T is
+//     stored in LDS in that key order, so no shuffle is needed.  The row
+//     sum is taken over the same rounded weights with v_dot2_f32_bf16.
+//   * Software pipeline, one key tile t per iteration:
+//       X: S(t+1) = K(t+1) Q^T (MFMA)  interleaved with  exp/convert/sum of S(t)
+//       Y: O += V(t)^T P(t)   (MFMA)  interleaved with  row max of S(t+1),
+//          LDS stores of K(t+2) and V(t+1), global loads of K(t+3), V(t+2)
+//     K and V^T tiles are double-buffered in LDS with one barrier per tile.
+//     Tiles past the sequence end are read through a buffer resource that
+//     ends at the sequence end, so they load as zeros with no per-lane test;
+//     scores of keys past the end are set to -inf in the last real tile.
 //   * Workgroups are remapped so each XCD works through a contiguous range
 //     of (batch, head, query tile), keeping that head's K/V hot in its L2.
 //
 // f32 path (small problems and parity): a plain VALU kernel, a few lanes per
 // query, K/V tiles staged through LDS, exact expf online softmax.
+#include <type_traits>
+
 #include "vx_device.h"
+
+#ifndef VX_FA_WAVES
+#define VX_FA_WAVES 8
+#endif
 
 namespace vx {
 
@@ -53,24 +71,25 @@ struct FaArgs {
 
 // ---------------------------------------------------------------- bf16 MFMA
 
-constexpr int FA_BR = 128;   // query rows per workgroup
 constexpr int FA_BC = 64;    // keys per tile
-constexpr int FA_PADK = 8;   // LDS row padding of K (elements)
-constexpr int FA_PADV = 8;   // LDS row padding of V^T (elements)
-
-template <int D>
-struct FaShape {
-    static constexpr int KROW = D + FA_PADK;            // K row pitch in LDS
-    static constexpr int VROW = FA_BC + FA_PADV;        // V^T row pitch in LDS
-    static constexpr int KS = FA_BC * KROW;             // K tile elements
-    static constexpr int VS = D * VROW;                 // V^T tile elements
-    static constexpr int STAGE = KS + VS;
-    static constexpr int KCH = FA_BC * D / 8 / 256;     // 16-byte K chunks per thread
-    static constexpr int DQ = D / 4;                    // V: 4-wide d groups
-    static constexpr int KPT = FA_BC * D / 4 / 256;     // V: keys per thread
-};
+constexpr int FA_PAD = 8;    // LDS row padding of K and V^T (elements)
+constexpr int FA_WAVES = VX_FA_WAVES;
 
 typedef float f32x8_t __attribute__((ext_vector_type(8)));
+
+template <int D, int WAVES>
+struct FaShape {
+    static constexpr int NT = 64 * WAVES;            // threads per workgroup
+    static constexpr int BR = 32 * WAVES;            // query rows per workgroup
+    static constexpr int KROW = D + FA_PAD;          // K row pitch in LDS
+    static constexpr int VROW = FA_BC + FA_PAD;      // V^T row pitch in LDS
+    static constexpr int KS = FA_BC * KROW;          // K tile elements
+    static constexpr int VS = D * VROW;              // V^T tile elements
+    static constexpr int KCH = FA_BC * D / 8 / NT;   // 16-byte K chunks per thread
+    static constexpr int DQ = D / 4;                 // V: 4-wide d groups
+    static constexpr int KPT = FA_BC * D / 4 / NT;   // V: keys per thread
+    static_assert(KCH >= 1 && KPT >= 2 && KPT % 2 == 0 && KPT <= 8, "tile does not divide");
+};
 
 // Key order inside each group of 16 keys as the S^T accumulator hands them
 // to the P^T operand: lanes 0-31 carry keys {0-3, 8-11}, lanes 32-63 carry
@@ -103,10 +122,32 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, 
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, 0x00020000);
 }
 
-// A lazily rescaled running maximum may trail the true one by up to this
-// many powers of two before the accumulator is rescaled (weights <= 2^8).
+// The running maximum may trail a row's true maximum by up to this many
+// powers of two before the accumulator is rescaled (weights <= 2^8).
 constexpr float FA_LAZY_LOG2 = 8.0f;
 
+// Bytes {lo halves} or {hi halves} of two words, as one word: v_perm_b32.
+__device__ __forceinline__ uint32_t pick_lo16(uint32_t a0, uint32_t a1) {
+    return __builtin_amdgcn_perm(a1, a0, 0x05040100u);
+}
+__device__ __forceinline__ uint32_t pick_hi16(uint32_t a0, uint32_t a1) {
+    return __builtin_amdgcn_perm(a1, a0, 0x07060302u);
+}
+
+// Sum of the 8 bf16 values of v, added to acc (v_dot2_f32_bf16 against 1.0).
+__device__ __forceinline__ float sum_bf16x8(bf16x8_t v, float acc) {
+    const u32x4_t w = __builtin_bit_cast(u32x4_t, v);
+    const bf16x2_t one = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w[i]), one, acc, false);
+    return acc;
+}
+
+// Q fragment of one query row as the B operand of S^T = K Q^T: element
+// (ks, e) is column ks * 16 + g * 8 + e.  The row is optionally rotated by
+// the 3D RoPE (rounded to bf16, exactly as vx_rope3d_apply stores it), then
+// multiplied by scale * log2(e) and rounded to bf16.
 template <int D>
 __device__ __forceinline__ void load_q_fragment(const FaArgs& a, const uint16_t* qb, int64_t qi,
                                                 int g, bf16x8_t* qf) {
@@ -114,8 +155,8 @@ __device__ __forceinline__ void load_q_fragment(const FaArgs& a, const uint16_t*
     for (int ks = 0; ks < D / 16; ++ks) {
         uint4 w = {0u, 0u, 0u, 0u};
         if (qi < a.n) w = *(const uint4*)(qb + qi * a.row_stride + ks * 16 + g * 8);
+        uint32_t u[4] = {w.x, w.y, w.z, w.w};
         if (a.use_rope && qi < a.n) {
-            uint32_t u[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
                 const int pair = (ks * 16 + g * 8) / 2 + m;
@@ -128,17 +169,24 @@ __device__ __forceinline__ void load_q_fragment(const FaArgs& a, const uint16_t*
                     u[m] = pack_bf16x2(x0, x1);
                 }
             }
-            w = uint4{u[0], u[1], u[2], u[3]};
         }
-        qf[ks] = __builtin_bit_cast(bf16x8_t, w);
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+            u[m] = pack_bf16x2(bf16_lo(u[m]) * a.scale_log2, bf16_hi(u[m]) * a.scale_log2);
+        qf[ks] = __builtin_bit_cast(bf16x8_t, uint4{u[0], u[1], u[2], u[3]});
     }
 }
 
-template <int D>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
+template <int D, int WAVES>
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * WAVES, 64 * WAVES),
+                          amdgpu_waves_per_eu(2, 2)))
 void fa_fwd_bf16_kernel(FaArgs a) {
-    using S = FaShape<D>;
-    __shared__ __attribute__((aligned(16))) uint16_t lds[2 * S::STAGE];
+    using S = FaShape<D, WAVES>;
+    constexpr int NKK = D / 16;      // MFMA k-steps of one S^T block
+    constexpr int NDB = D / 32;      // 32-row blocks of O^T
+    __shared__ __attribute__((aligned(16))) uint16_t lds[2 * S::KS + 2 * S::VS];
+    uint16_t* const kbuf[2] = {lds, lds + S::KS};
+    uint16_t* const vbuf[2] = {lds + 2 * S::KS, lds + 2 * S::KS + S::VS};
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63, l32 = lane & 31, g = lane >> 5;
@@ -149,19 +197,18 @@ void fa_fwd_bf16_kernel(FaArgs a) {
     const int h = (int)(bh % a.heads);
     const int64_t b = bh / a.heads;
     const int64_t off = b * a.batch_stride + (int64_t)h * D;
-    const uint16_t* qb = a.q + off;
     const uint16_t* kb = a.k + off;
     const uint16_t* vb = a.v + off;
     const int64_t n = a.n;
+    const int nt = (int)((n + FA_BC - 1) / FA_BC);
 
-    const int64_t qi = (int64_t)qt * FA_BR + wave * 32 + l32;
-    bf16x8_t qf[D / 16];
-    load_q_fragment<D>(a, qb, qi, g, qf);
+    const int64_t qi = (int64_t)qt * S::BR + wave * 32 + l32;
+    bf16x8_t qf[NKK];
+    load_q_fragment<D>(a, a.q + off, qi, g, qf);
 
-    // ---- tile staging: global -> registers -> LDS
-    // Each thread's byte offsets inside a tile are fixed; the tile start
-    // and the sequence end live in a per-tile scalar buffer resource, so
-    // keys past the end read as zero without any per-lane bounds test.
+    // ---- tile staging: global -> registers -> LDS.  Each thread's byte
+    // offsets inside a tile are fixed; the tile start and the sequence end
+    // live in a per-tile scalar buffer resource.
     u32x4_t kreg[S::KCH];
     uint2 vreg[S::KPT];
     const int vdq = tid % S::DQ, vkg = tid / S::DQ;
@@ -169,144 +216,220 @@ void fa_fwd_bf16_kernel(FaArgs a) {
     uint32_t koff[S::KCH], voff[S::KPT];
 #pragma unroll
     for (int i = 0; i < S::KCH; ++i) {
-        const int c = tid + 256 * i;
+        const int c = tid + S::NT * i;
         koff[i] = (uint32_t)((c / (D / 8)) * row_bytes + (c % (D / 8)) * 16);
     }
 #pragma unroll
     for (int s = 0; s < S::KPT; ++s)
         voff[s] = (uint32_t)(swap_bits23(vkg * S::KPT + s) * row_bytes + vdq * 8);
 
-    auto load_tile = [&](int64_t kv0) {
-        const int64_t left = (n - kv0) * row_bytes;
-        const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(kb + kv0 * a.row_stride, left);
-        const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(vb + kv0 * a.row_stride, left);
+    auto load_k = [&](int t) {
+        const int64_t kv0 = (int64_t)t * FA_BC;
+        const __amdgpu_buffer_rsrc_t r = buffer_rsrc(kb + kv0 * a.row_stride, (n - kv0) * row_bytes);
 #pragma unroll
-        for (int i = 0; i < S::KCH; ++i)
-            kreg[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, koff[i], 0, 0);
+        for (int i = 0; i < S::KCH; ++i) kreg[i] = __builtin_amdgcn_raw_buffer_load_b128(r, koff[i], 0, 0);
+    };
+    auto load_v = [&](int t) {
+        const int64_t kv0 = (int64_t)t * FA_BC;
+        const __amdgpu_buffer_rsrc_t r = buffer_rsrc(vb + kv0 * a.row_stride, (n - kv0) * row_bytes);
 #pragma unroll
         for (int s = 0; s < S::KPT; ++s) {
-            const auto w = __builtin_amdgcn_raw_buffer_load_b64(rv, voff[s], 0, 0);
+            const auto w = __builtin_amdgcn_raw_buffer_load_b64(r, voff[s], 0, 0);
             vreg[s] = uint2{w[0], w[1]};
         }
     };
-    auto store_tile = [&](int buf) {
-        uint16_t* ks = lds + buf * S::STAGE;
-        uint16_t* vt = ks + S::KS;
+    auto store_k_chunk = [&](uint16_t* ks, int i) {
+        const int c = tid + S::NT * i;
+        *(u32x4_t*)(ks + (c / (D / 8)) * S::KROW + (c % (D / 8)) * 8) = kreg[i];
+    };
+    auto store_k = [&](uint16_t* ks) {
 #pragma unroll
-        for (int i = 0; i < S::KCH; ++i) {
-            const int c = tid + 256 * i;
-            const int key = c / (D / 8), col = c % (D / 8);
-            *(u32x4_t*)(ks + key * S::KROW + col * 8) = kreg[i];
+        for (int i = 0; i < S::KCH; ++i) store_k_chunk(ks, i);
+    };
+    // transpose: element j of each of the KPT keys -> one V^T row segment
+    auto store_v_row = [&](uint16_t* vt, int j) {
+        uint32_t w[S::KPT / 2];
+#pragma unroll
+        for (int s = 0; s < S::KPT; s += 2) {
+            const uint32_t a0 = (j < 2) ? vreg[s].x : vreg[s].y;
+            const uint32_t a1 = (j < 2) ? vreg[s + 1].x : vreg[s + 1].y;
+            w[s / 2] = (j & 1) ? pick_hi16(a0, a1) : pick_lo16(a0, a1);
         }
-        // transpose: element j of each of the KPT keys -> one V^T row segment
+        uint16_t* dst = vt + (vdq * 4 + j) * S::VROW + vkg * S::KPT;
+        if constexpr (S::KPT == 8) *(uint4*)dst = uint4{w[0], w[1], w[2], w[3]};
+        else if constexpr (S::KPT == 4) *(uint2*)dst = uint2{w[0], w[1]};
+        else *(uint32_t*)dst = w[0];
+    };
+    auto store_v = [&](uint16_t* vt) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            uint32_t w[S::KPT / 2];
-#pragma unroll
-            for (int s = 0; s < S::KPT; s += 2) {
-                const uint32_t a0 = (j < 2) ? vreg[s].x : vreg[s].y;
-                const uint32_t a1 = (j < 2) ? vreg[s + 1].x : vreg[s + 1].y;
-                w[s / 2] = (j & 1) ? ((a0 >> 16) | (a1 & 0xffff0000u))
-                                   : ((a0 & 0xffffu) | (a1 << 16));
-            }
-            uint16_t* dst = vt + (vdq * 4 + j) * S::VROW + vkg * S::KPT;
-            if constexpr (S::KPT == 8) *(uint4*)dst = uint4{w[0], w[1], w[2], w[3]};
-            else *(uint2*)dst = uint2{w[0], w[1]};
-        }
+        for (int j = 0; j < 4; ++j) store_v_row(vt, j);
     };
 
-    f32x16_t acc[D / 32];
-#pragma unroll
-    for (int i = 0; i < D / 32; ++i) acc[i] = f32x16_t{};
-    float m_run = -__builtin_inff();   // running row max, raw score units
-    float l_run = 0.f;                 // this lane's share of the row sum
-
-    const int nt = (int)((n + FA_BC - 1) / FA_BC);
-    load_tile(0);
-    store_tile(0);
-    __syncthreads();
-
-    for (int t = 0; t < nt; ++t) {
-        const int buf = t & 1;
-        const uint16_t* ks = lds + buf * S::STAGE;
-        const uint16_t* vt = ks + S::KS;
-        if (t + 1 < nt) load_tile((int64_t)(t + 1) * FA_BC);
-
-        // S^T = K . Q^T for two blocks of 32 keys
-        f32x16_t st[2];
+    // S^T(t) - m for both 32-key blocks of a tile held in LDS at ks
+    auto scores = [&](f32x16_t* s, const uint16_t* ks, const f32x16_t& negm) {
 #pragma unroll
         for (int kb2 = 0; kb2 < 2; ++kb2) {
-            st[kb2] = f32x16_t{};
 #pragma unroll
-            for (int kk = 0; kk < D / 16; ++kk) {
+            for (int kk = 0; kk < NKK; ++kk) {
                 const bf16x8_t av = *(const bf16x8_t*)(ks + (kb2 * 32 + l32) * S::KROW + kk * 16 + g * 8);
-                st[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qf[kk], st[kb2], 0, 0, 0);
+                s[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qf[kk], kk == 0 ? negm : s[kb2], 0, 0, 0);
             }
         }
-
-        // keys past the end of the sequence take no weight
+    };
+    auto mask_tail = [&](f32x16_t* s, int t) {
         const int64_t kv0 = (int64_t)t * FA_BC;
-        if (kv0 + FA_BC > n) {
-#pragma unroll
-            for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int64_t key = kv0 + kb2 * 32 + 8 * (i >> 2) + 4 * g + (i & 3);
-                    if (key >= n) st[kb2][i] = -__builtin_inff();
-                }
-        }
-
-        float mx = st[0][0];
-#pragma unroll
-        for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, st[kb2][i]);
-        mx = half_max(mx);
-        // Rescale only when some row's maximum outgrew the reference by more
-        // than 2^FA_LAZY_LOG2 (always on the first tile, where m_run = -inf).
-        if (__builtin_amdgcn_ballot_w64((mx - m_run) * a.scale_log2 > FA_LAZY_LOG2) != 0) {
-            const float m_new = fmaxf(m_run, mx);
-            const float alpha = fast_exp2((m_run - m_new) * a.scale_log2);
-            m_run = m_new;
-            l_run *= alpha;
-#pragma unroll
-            for (int i = 0; i < D / 32; ++i) acc[i] *= alpha;
-        }
-        const float mb = m_run * a.scale_log2;
-
-        float psum = 0.f;
 #pragma unroll
         for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                const float p = fast_exp2(__builtin_fmaf(st[kb2][i], a.scale_log2, -mb));
-                st[kb2][i] = p;
-                psum += p;
+                const int64_t key = kv0 + kb2 * 32 + 8 * (i >> 2) + 4 * g + (i & 3);
+                if (key >= n) s[kb2][i] = -__builtin_inff();
             }
-        l_run += psum;
+    };
+    auto row_max = [&](const f32x16_t* s) {
+        float mx = fmaxf(s[0][0], s[1][0]);
+#pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+            for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[kb2][i]);
+        return half_max(mx);
+    };
 
-        // P^T operand: 16 keys per MFMA, taken from accumulator slots 0-7 / 8-15
+    f32x16_t acc[NDB];
+#pragma unroll
+    for (int i = 0; i < NDB; ++i) acc[i] = f32x16_t{};
+    f32x16_t negm = f32x16_t{};   // -m in every slot: the C operand of the first k-step
+    float m_ref = 0.f;            // running reference maximum (base-2 units)
+    float l_run = 0.f;            // this lane's share of the row sum
+    const bool tail = (n % FA_BC) != 0;
+
+    // ---- prologue: K(0), V(0), K(1) into LDS; S(0); m from tile 0
+    f32x16_t sA[2], sB[2];
+    load_k(0);
+    load_v(0);
+    store_k(kbuf[0]);
+    store_v(vbuf[0]);
+    load_k(1);
+    store_k(kbuf[1]);
+    __syncthreads();
+    scores(sA, kbuf[0], negm);
+    __syncthreads();              // kbuf[0] is refilled in the first iteration
+    load_k(2);
+    load_v(1);
+    if (nt == 1 && tail) mask_tail(sA, 0);
+    {
+        const float mx = row_max(sA);
+        m_ref = mx;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            negm[i] = -m_ref;
+            sA[0][i] -= mx;
+            sA[1][i] -= mx;
+        }
+    }
+    float mx_next = 0.f;
+
+    // One key tile.  sc holds S(t) - m (already rescaled), sn receives S(t+1).
+    // One key tile.  sc holds S(t) - m (already rescaled), sn receives
+    // S(t+1).  The two halves are written out in issue order: every group
+    // below pairs one MFMA with the VALU, LDS and global-memory work that
+    // is to run under it, and sched_barrier(0) keeps the groups in order.
+    auto step = [&](auto parity, f32x16_t* sc, f32x16_t* sn, int t) {
+        constexpr int P = decltype(parity)::value;
+        constexpr int NX = 2 * NKK;          // MFMAs of S(t+1)
+        constexpr int WPM = 16 / NX;         // P words (2 weights each) per MFMA
+        constexpr int NY = NDB * FA_BC / 16; // MFMAs of P V
+        constexpr int MPM = 32 / (NY / 2);   // scores per MFMA in the row max
+        // ---- X: S(t+1) = K(t+1) Q^T - m  ||  P(t) = 2^(S(t) - m), its row sum
+        const uint16_t* ks = kbuf[P ^ 1] + l32 * S::KROW + g * 8;
+        auto kfrag = [&](int i) {
+            return *(const bf16x8_t*)(ks + (i / NKK) * 32 * S::KROW + (i % NKK) * 16);
+        };
+        const uint16_t* vt = vbuf[P] + l32 * S::VROW + g * 8;
+        auto vfrag = [&](int i) {
+            return *(const bf16x8_t*)(vt + (i / 4) * 32 * S::VROW + (i % 4) * 16);
+        };
+        bf16x8_t kf[3], vf[3];
+        kf[0] = kfrag(0);
+        kf[1] = kfrag(1);
+        uint32_t pw[16];
+        float psum = l_run;
+        const bf16x2_t one = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+        for (int i = 0; i < NX; ++i) {
+            if (i + 2 < NX) kf[(i + 2) % 3] = kfrag(i + 2);
+            const int kb2 = i / NKK, kk = i % NKK;
+            sn[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i % 3], qf[kk],
+                                                              kk == 0 ? negm : sn[kb2], 0, 0, 0);
+#pragma unroll
+            for (int e = 0; e < WPM; ++e) {
+                const int w = i * WPM + e;   // weights 2w, 2w+1: scores (2w) / 16, (2w) % 16
+                const float p0 = fast_exp2(sc[(2 * w) >> 4][(2 * w) & 15]);
+                const float p1 = fast_exp2(sc[(2 * w + 1) >> 4][(2 * w + 1) & 15]);
+                pw[w] = pack_bf16x2(p0, p1);
+                psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pw[w]), one,
+                                                       psum, false);
+            }
+            if (i + 2 == NX) vf[0] = vfrag(0);
+            if (i + 1 == NX) vf[1] = vfrag(1);
+            __asm__ volatile("" ::"v"(psum));   // keep the row sum in this group
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        l_run = psum;
         bf16x8_t pb[FA_BC / 16];
 #pragma unroll
-        for (int kk = 0; kk < FA_BC / 16; ++kk) {
-            const f32x16_t& src = st[kk >> 1];
-            const int o8 = (kk & 1) * 8;
-            f32x8_t f = {src[o8 + 0], src[o8 + 1], src[o8 + 2], src[o8 + 3],
-                         src[o8 + 4], src[o8 + 5], src[o8 + 6], src[o8 + 7]};
-            pb[kk] = __builtin_convertvector(f, bf16x8_t);
-        }
-
-        // O^T += V^T . P^T
+        for (int kk = 0; kk < FA_BC / 16; ++kk)
+            pb[kk] = __builtin_bit_cast(bf16x8_t, u32x4_t{pw[4 * kk], pw[4 * kk + 1],
+                                                          pw[4 * kk + 2], pw[4 * kk + 3]});
+        // ---- Y: O += V(t)^T P(t)  ||  K(t+2), V(t+1) into LDS; loads of
+        // K(t+3), V(t+2); row max of S(t+1)
+        float mx = -__builtin_inff();
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db)
+        for (int i = 0; i < NY; ++i) {
+            if (i + 2 < NY) vf[(i + 2) % 3] = vfrag(i + 2);
+            acc[i / 4] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i % 3], pb[i % 4], acc[i / 4],
+                                                                 0, 0, 0);
+            if (i < S::KCH) store_k_chunk(kbuf[P], i);
+            else if (i < S::KCH + 4) store_v_row(vbuf[P ^ 1], i - S::KCH);
+            else if (i == S::KCH + 4) load_k(t + 3);
+            else if (i == S::KCH + 5) load_v(t + 2);
+            if (i >= NY / 2) {
 #pragma unroll
-            for (int kk = 0; kk < FA_BC / 16; ++kk) {
-                const bf16x8_t av = *(const bf16x8_t*)(vt + (db * 32 + l32) * S::VROW + kk * 16 + g * 8);
-                acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[kk], acc[db], 0, 0, 0);
+                for (int e = 0; e < MPM; ++e) {
+                    const int j = (i - NY / 2) * MPM + e;
+                    mx = fmaxf(mx, sn[j >> 4][j & 15]);
+                }
             }
-
-        if (t + 1 < nt) store_tile(buf ^ 1);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        mx_next = half_max(mx);
         __syncthreads();
+        // ---- the last real tile: keys past the end take no weight
+        if (t + 1 == nt - 1 && tail) {
+            mask_tail(sn, t + 1);
+            mx_next = row_max(sn);
+        }
+        // ---- lazy rescale for S(t+1) (rare after the first tiles)
+        if (t + 1 < nt && __builtin_amdgcn_ballot_w64(mx_next > FA_LAZY_LOG2) != 0) {
+            const float delta = fmaxf(mx_next, 0.f);
+            const float alpha = fast_exp2(-delta);
+            m_ref += delta;
+            l_run *= alpha;
+#pragma unroll
+            for (int i = 0; i < NDB; ++i) acc[i] *= alpha;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                negm[i] = -m_ref;
+                sn[0][i] -= delta;
+                sn[1][i] -= delta;
+            }
+        }
+    };
+
+    for (int t = 0; t < nt; t += 2) {
+        step(std::integral_constant<int, 0>{}, sA, sB, t);
+        if (t + 1 >= nt) break;
+        step(std::integral_constant<int, 1>{}, sB, sA, t + 1);
     }
 
     // epilogue: combine the two halves' row sums, normalise, store
@@ -315,7 +438,7 @@ void fa_fwd_bf16_kernel(FaArgs a) {
     if (qi < n) {
         uint16_t* ob = a.o + off + qi * a.row_stride;
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db)
+        for (int db = 0; db < NDB; ++db)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const f32x16_t& c = acc[db];
@@ -325,7 +448,7 @@ void fa_fwd_bf16_kernel(FaArgs a) {
                 *(uint2*)(ob + db * 32 + 8 * r + 4 * g) = w;
             }
         if (a.lse != nullptr && g == 0)
-            a.lse[bh * n + qi] = m_run * a.scale + logf(l_tot);
+            a.lse[bh * n + qi] = (m_ref + __builtin_log2f(l_tot)) * 0.69314718055994531f;
     }
 }
 
@@ -420,6 +543,7 @@ void fa_fwd_f32_kernel(FaArgs a) {
     }
 }
 
+
 // ---------------------------------------------------------------- launch
 
 hipError_t launch_flash_attn(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -441,18 +565,25 @@ hipError_t launch_flash_attn(const void* q, const void* k, const void* v, void* 
     if (rope) a.rope = *rope;
     else a.rope = RopeArgs{1, 1, 1, 0, 0, 0, 0, 1.f};
 
-    const int rows_per_wg = bf16 ? FA_BR : 256 / (int)(head_dim / 32);
+    const int rows_per_wg = bf16 ? 32 * FA_WAVES : 256 / (int)(head_dim / 32);
     a.n_qtiles = (int)((n + rows_per_wg - 1) / rows_per_wg);
     a.total_tiles = batch * heads * a.n_qtiles;
-    const dim3 grid((unsigned)a.total_tiles), block(256);
+    const dim3 grid((unsigned)a.total_tiles);
     if (bf16) {
-        if (head_dim == 128) hipLaunchKernelGGL(fa_fwd_bf16_kernel<128>, grid, block, 0, st, a);
-        else hipLaunchKernelGGL(fa_fwd_bf16_kernel<64>, grid, block, 0, st, a);
+        const dim3 block(64 * FA_WAVES);
+        if (head_dim == 128) hipLaunchKernelGGL((fa_fwd_bf16_kernel<128, FA_WAVES>), grid, block, 0, st, a);
+        else hipLaunchKernelGGL((fa_fwd_bf16_kernel<64, FA_WAVES>), grid, block, 0, st, a);
     } else {
+        const dim3 block(256);
         if (head_dim == 128) hipLaunchKernelGGL(fa_fwd_f32_kernel<128>, grid, block, 0, st, a);
         else hipLaunchKernelGGL(fa_fwd_f32_kernel<64>, grid, block, 0, st, a);
     }
     return hipGetLastError();
+}
+
+// Query rows one bf16 workgroup covers (the host sizes the grid with it).
+int flash_attn_rows_per_workgroup(bool bf16, int64_t head_dim) {
+    return bf16 ? 32 * FA_WAVES : 256 / (int)(head_dim / 32);
 }
 
 }  // namespace vx

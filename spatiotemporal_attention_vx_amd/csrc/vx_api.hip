@@ -20,6 +20,7 @@ hipError_t launch_rope3d(void* q, void* k, int64_t batch, int64_t n_tokens, int6
 hipError_t launch_flash_attn(const void* q, const void* k, const void* v, void* o, float* lse,
                              int64_t batch, int64_t n, int64_t heads, int64_t head_dim,
                              float scale, const RopeArgs* rope, bool bf16, hipStream_t st);
+int flash_attn_rows_per_workgroup(bool bf16, int64_t head_dim);
 }  // namespace vx
 
 namespace {
@@ -178,7 +179,7 @@ int vx_flash_attn_fwd(const void* q, const void* k, const void* v, void* o, floa
     const bool bf16 = dt == VX_BF16;
     const int64_t esz = bf16 ? 2 : 4;
     int64_t bytes, lse_bytes, rows;
-    const int64_t per_wg = bf16 ? 128 : 256 / (head_dim / 32);
+    const int64_t per_wg = vx::flash_attn_rows_per_workgroup(bf16, head_dim);
     if (!mul_ok(bytes, {batch, n_tokens, heads, head_dim, esz}) ||
         !mul_ok(lse_bytes, {batch, heads, n_tokens, 4}) ||
         !mul_ok(rows, {batch, heads, (n_tokens + per_wg - 1) / per_wg}) || rows > INT32_MAX)

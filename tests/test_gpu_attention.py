@@ -9,14 +9,15 @@ from spatiotemporal_attention_vx_amd import binding, configs, inputs
 
 pytestmark = pytest.mark.gpu
 
-# The bf16 LSE: scores are fp32 sums of exact bf16 products, so the error is
-# a few fp32 ulps of |s| times the log-sum-exp's sensitivity (<= 1).
-LSE_TOL = {"f32": 1e-5, "bf16": 1e-4}
-# After RoPE the rotated Q and K are stored in bf16 (relative rounding up to
-# 2^-9 per element) while the oracle rotates in fp64.  A score then moves by
-# about scale * sqrt(2 d) * 2^-9 / sqrt(3) ~ 1.6e-3 (RMS, d = 128, unit
-# inputs); the LSE, a softmax-weighted mean of score moves, stays within a
-# few of those.
+# The bf16 kernel multiplies Q by scale * log2(e) as it loads it and keeps
+# the product in bf16 (relative rounding up to 2^-9 per element), so a score
+# moves by about scale * sqrt(d) * 2^-9 / sqrt(3) ~ 1.1e-3 (RMS, unit
+# inputs).  The LSE is a softmax-weighted mean of those moves: at most one
+# score's move (N = 1), a few RMS in the worst case.
+LSE_TOL = {"f32": 1e-5, "bf16": 1e-2}
+# After RoPE the rotated Q and K are also stored in bf16 while the oracle
+# rotates in fp64: another move of about scale * sqrt(2 d) * 2^-9 / sqrt(3)
+# ~ 1.6e-3 RMS per score, still within the same bound.
 LSE_TOL_ROPE = {"f32": 1e-5, "bf16": 1e-2}
 
 
