@@ -126,6 +126,12 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, 
 // powers of two before the accumulator is rescaled (weights <= 2^8).
 constexpr float FA_LAZY_LOG2 = 8.0f;
 
+// V^T rows are stored with their 16-byte chunks permuted: chunk c of row r
+// sits at chunk c ^ vswz(r).  The transposing stores then write rows 4 apart
+// to 16 distinct bank groups, and a fragment read (16 consecutive rows, one
+// chunk) still covers every bank group once.
+__device__ __forceinline__ int vswz(int row) { return (row >> 4) & 3; }
+
 // Bytes {lo halves} or {hi halves} of two words, as one word: v_perm_b32.
 __device__ __forceinline__ uint32_t pick_lo16(uint32_t a0, uint32_t a1) {
     return __builtin_amdgcn_perm(a1, a0, 0x05040100u);
@@ -255,7 +261,8 @@ void fa_fwd_bf16_kernel(FaArgs a) {
             const uint32_t a1 = (j < 2) ? vreg[s + 1].x : vreg[s + 1].y;
             w[s / 2] = (j & 1) ? pick_hi16(a0, a1) : pick_lo16(a0, a1);
         }
-        uint16_t* dst = vt + (vdq * 4 + j) * S::VROW + vkg * S::KPT;
+        const int row = vdq * 4 + j, pos = vkg * S::KPT;
+        uint16_t* dst = vt + row * S::VROW + (((pos >> 3) ^ vswz(row)) << 3) + (pos & 7);
         if constexpr (S::KPT == 8) *(uint4*)dst = uint4{w[0], w[1], w[2], w[3]};
         else if constexpr (S::KPT == 4) *(uint2*)dst = uint2{w[0], w[1]};
         else *(uint32_t*)dst = w[0];
@@ -345,9 +352,12 @@ void fa_fwd_bf16_kernel(FaArgs a) {
         auto kfrag = [&](int i) {
             return *(const bf16x8_t*)(ks + (i / NKK) * 32 * S::KROW + (i % NKK) * 16);
         };
-        const uint16_t* vt = vbuf[P] + l32 * S::VROW + g * 8;
+        // row db*32 + l32 of V^T, 16-byte chunk 2kk + g, stored at chunk
+        // (2kk + g) ^ vswz(row) = (2kk ^ (2db & 3)) + (g ^ (l32 >> 4))
+        const uint16_t* vt = vbuf[P] + l32 * S::VROW + ((g ^ (l32 >> 4)) << 3);
         auto vfrag = [&](int i) {
-            return *(const bf16x8_t*)(vt + (i / 4) * 32 * S::VROW + (i % 4) * 16);
+            const int db = i / 4, kk = i % 4;
+            return *(const bf16x8_t*)(vt + db * 32 * S::VROW + (((2 * kk) ^ ((2 * db) & 3)) << 3));
         };
         bf16x8_t kf[3], vf[3];
         kf[0] = kfrag(0);
@@ -417,9 +427,12 @@ void fa_fwd_bf16_kernel(FaArgs a) {
             l_run *= alpha;
 #pragma unroll
             for (int i = 0; i < NDB; ++i) acc[i] *= alpha;
+            // -m is rewritten in place: a plain assignment here makes the
+            // register allocator copy the block on every tile.
+            const float nm = -m_ref;
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                negm[i] = -m_ref;
+                __asm__ volatile("v_mov_b32 %0, %1" : "+v"(negm[i]) : "v"(nm));
                 sn[0][i] -= delta;
                 sn[1][i] -= delta;
             }
