@@ -48,6 +48,12 @@
 #ifndef VX_FA_WAVES
 #define VX_FA_WAVES 8
 #endif
+#ifndef VX_FA_QG
+#define VX_FA_QG 1
+#endif
+#ifndef VX_FA_DMA
+#define VX_FA_DMA 1
+#endif
 
 namespace vx {
 
@@ -73,14 +79,15 @@ struct FaArgs {
 
 constexpr int FA_BC = 64;    // keys per tile
 constexpr int FA_PAD = 8;    // LDS row padding of K and V^T (elements)
-constexpr int FA_WAVES = VX_FA_WAVES;
+constexpr int FA_WAVES = VX_FA_WAVES;   // waves per workgroup
+constexpr int FA_QG = VX_FA_QG;         // 32-row query groups per wave
 
 typedef float f32x8_t __attribute__((ext_vector_type(8)));
 
-template <int D, int WAVES>
+template <int D, int WAVES, int QG>
 struct FaShape {
     static constexpr int NT = 64 * WAVES;            // threads per workgroup
-    static constexpr int BR = 32 * WAVES;            // query rows per workgroup
+    static constexpr int BR = 32 * QG * WAVES;       // query rows per workgroup
     static constexpr int KROW = D + FA_PAD;          // K row pitch in LDS
     static constexpr int VROW = FA_BC + FA_PAD;      // V^T row pitch in LDS
     static constexpr int KS = FA_BC * KROW;          // K tile elements
@@ -183,16 +190,16 @@ __device__ __forceinline__ void load_q_fragment(const FaArgs& a, const uint16_t*
     }
 }
 
-template <int D, int WAVES>
+template <int D, int WAVES, int QG>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * WAVES, 64 * WAVES),
-                          amdgpu_waves_per_eu(2, 2)))
+                          amdgpu_waves_per_eu(3 - QG, 3 - QG)))
 void fa_fwd_bf16_kernel(FaArgs a) {
-    using S = FaShape<D, WAVES>;
+    using S = FaShape<D, WAVES, QG>;
     constexpr int NKK = D / 16;      // MFMA k-steps of one S^T block
     constexpr int NDB = D / 32;      // 32-row blocks of O^T
-    __shared__ __attribute__((aligned(16))) uint16_t lds[2 * S::KS + 2 * S::VS];
-    uint16_t* const kbuf[2] = {lds, lds + S::KS};
-    uint16_t* const vbuf[2] = {lds + 2 * S::KS, lds + 2 * S::KS + S::VS};
+    __shared__ __attribute__((aligned(16))) uint16_t lds[3 * S::KS + 2 * S::VS];
+    uint16_t* const kbuf[3] = {lds, lds + S::KS, lds + 2 * S::KS};
+    uint16_t* const vbuf[2] = {lds + 3 * S::KS, lds + 3 * S::KS + S::VS};
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63, l32 = lane & 31, g = lane >> 5;
@@ -208,9 +215,14 @@ void fa_fwd_bf16_kernel(FaArgs a) {
     const int64_t n = a.n;
     const int nt = (int)((n + FA_BC - 1) / FA_BC);
 
-    const int64_t qi = (int64_t)qt * S::BR + wave * 32 + l32;
-    bf16x8_t qf[NKK];
-    load_q_fragment<D>(a, a.q + off, qi, g, qf);
+    // query group qg of this wave: rows (wave * QG + qg) * 32 + l32 of the tile
+    int64_t qi[QG];
+    bf16x8_t qf[QG][NKK];
+#pragma unroll
+    for (int qg = 0; qg < QG; ++qg) {
+        qi[qg] = (int64_t)qt * S::BR + (wave * QG + qg) * 32 + l32;
+        load_q_fragment<D>(a, a.q + off, qi[qg], g, qf[qg]);
+    }
 
     // ---- tile staging: global -> registers -> LDS.  Each thread's byte
     // offsets inside a tile are fixed; the tile start and the sequence end
@@ -272,14 +284,14 @@ void fa_fwd_bf16_kernel(FaArgs a) {
         for (int j = 0; j < 4; ++j) store_v_row(vt, j);
     };
 
-    // S^T(t) - m for both 32-key blocks of a tile held in LDS at ks
-    auto scores = [&](f32x16_t* s, const uint16_t* ks, const f32x16_t& negm) {
+    // S^T - m of one query group for both 32-key blocks of the tile at ks
+    auto scores = [&](f32x16_t* s, const uint16_t* ks, const bf16x8_t* q, const f32x16_t& negm) {
 #pragma unroll
         for (int kb2 = 0; kb2 < 2; ++kb2) {
 #pragma unroll
             for (int kk = 0; kk < NKK; ++kk) {
                 const bf16x8_t av = *(const bf16x8_t*)(ks + (kb2 * 32 + l32) * S::KROW + kk * 16 + g * 8);
-                s[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qf[kk], kk == 0 ? negm : s[kb2], 0, 0, 0);
+                s[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, q[kk], kk == 0 ? negm : s[kb2], 0, 0, 0);
             }
         }
     };
@@ -302,122 +314,468 @@ void fa_fwd_bf16_kernel(FaArgs a) {
         return half_max(mx);
     };
 
-    f32x16_t acc[NDB];
+    f32x16_t acc[QG][NDB];
+    f32x16_t negm[QG];           // -m in every slot: the C operand of the first k-step
+    float m_ref[QG], l_run[QG], mx_next[QG];
 #pragma unroll
-    for (int i = 0; i < NDB; ++i) acc[i] = f32x16_t{};
-    f32x16_t negm = f32x16_t{};   // -m in every slot: the C operand of the first k-step
-    float m_ref = 0.f;            // running reference maximum (base-2 units)
-    float l_run = 0.f;            // this lane's share of the row sum
+    for (int qg = 0; qg < QG; ++qg) {
+#pragma unroll
+        for (int i = 0; i < NDB; ++i) acc[qg][i] = f32x16_t{};
+        negm[qg] = f32x16_t{};
+        l_run[qg] = 0.f;
+        mx_next[qg] = 0.f;
+    }
     const bool tail = (n % FA_BC) != 0;
 
-    // ---- prologue: K(0), V(0), K(1) into LDS; S(0); m from tile 0
-    f32x16_t sA[2], sB[2];
+    // ---- prologue: K(0), K(1), K(2) and V(0) into LDS; S(0); m from tile 0
+    f32x16_t sA[QG][2], sB[QG][2];
     load_k(0);
     load_v(0);
     store_k(kbuf[0]);
     store_v(vbuf[0]);
     load_k(1);
     store_k(kbuf[1]);
-    __syncthreads();
-    scores(sA, kbuf[0], negm);
-    __syncthreads();              // kbuf[0] is refilled in the first iteration
     load_k(2);
+    store_k(kbuf[2]);
+    __syncthreads();
+#pragma unroll
+    for (int qg = 0; qg < QG; ++qg) scores(sA[qg], kbuf[0], qf[qg], negm[qg]);
+    __syncthreads();              // kbuf[0] is refilled in the first iteration
+    load_k(3);
     load_v(1);
-    if (nt == 1 && tail) mask_tail(sA, 0);
-    {
-        const float mx = row_max(sA);
-        m_ref = mx;
+#pragma unroll
+    for (int qg = 0; qg < QG; ++qg) {
+        if (nt == 1 && tail) mask_tail(sA[qg], 0);
+        const float mx = row_max(sA[qg]);
+        m_ref[qg] = mx;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-            negm[i] = -m_ref;
-            sA[0][i] -= mx;
-            sA[1][i] -= mx;
+            negm[qg][i] = -mx;
+            sA[qg][0][i] -= mx;
+            sA[qg][1][i] -= mx;
         }
     }
-    float mx_next = 0.f;
 
-    // One key tile.  sc holds S(t) - m (already rescaled), sn receives S(t+1).
+    // Lane parts of the LDS fragment addresses.  K^T fragment i of a tile:
+    // rows (i / NKK) * 32 + l32, columns (i % NKK) * 16 + g * 8.  V^T
+    // fragment i: row (i / 4) * 32 + l32, 16-byte chunk 2 (i % 4) + g stored
+    // at chunk (2 (i % 4) + g) ^ vswz(row) = (2 (i % 4) ^ (2 (i / 4) & 3)) + (g ^ (l32 >> 4)).
+    const int klane = l32 * S::KROW + g * 8;
+    const int vlane = l32 * S::VROW + ((g ^ (l32 >> 4)) << 3);
+    auto kfrag = [&](const uint16_t* kt, int i) {
+        return *(const bf16x8_t*)(kt + klane + (i / NKK) * 32 * S::KROW + (i % NKK) * 16);
+    };
+    auto vfrag = [&](const uint16_t* vt, int i) {
+        const int db = i / 4, kk = i % 4;
+        return *(const bf16x8_t*)(vt + vlane + db * 32 * S::VROW + (((2 * kk) ^ ((2 * db) & 3)) << 3));
+    };
+    // K tiles rotate through three buffers (K(t+1) and K(t+2) are resident
+    // while K(t+3) is written), so the first K fragments of the next tile
+    // can be read before the barrier; V tiles use two.
+    bf16x8_t kf[3];
+    kf[0] = kfrag(kbuf[1], 0);
+    kf[1] = kfrag(kbuf[1], 1);
+
     // One key tile.  sc holds S(t) - m (already rescaled), sn receives
     // S(t+1).  The two halves are written out in issue order: every group
     // below pairs one MFMA with the VALU, LDS and global-memory work that
     // is to run under it, and sched_barrier(0) keeps the groups in order.
-    auto step = [&](auto parity, f32x16_t* sc, f32x16_t* sn, int t) {
-        constexpr int P = decltype(parity)::value;
-        constexpr int NX = 2 * NKK;          // MFMAs of S(t+1)
-        constexpr int WPM = 16 / NX;         // P words (2 weights each) per MFMA
-        constexpr int NY = NDB * FA_BC / 16; // MFMAs of P V
-        constexpr int MPM = 32 / (NY / 2);   // scores per MFMA in the row max
-        // ---- X: S(t+1) = K(t+1) Q^T - m  ||  P(t) = 2^(S(t) - m), its row sum
-        const uint16_t* ks = kbuf[P ^ 1] + l32 * S::KROW + g * 8;
-        auto kfrag = [&](int i) {
-            return *(const bf16x8_t*)(ks + (i / NKK) * 32 * S::KROW + (i % NKK) * 16);
-        };
-        // row db*32 + l32 of V^T, 16-byte chunk 2kk + g, stored at chunk
-        // (2kk + g) ^ vswz(row) = (2kk ^ (2db & 3)) + (g ^ (l32 >> 4))
-        const uint16_t* vt = vbuf[P] + l32 * S::VROW + ((g ^ (l32 >> 4)) << 3);
-        auto vfrag = [&](int i) {
-            const int db = i / 4, kk = i % 4;
-            return *(const bf16x8_t*)(vt + db * 32 * S::VROW + (((2 * kk) ^ ((2 * db) & 3)) << 3));
-        };
-        bf16x8_t kf[3], vf[3];
-        kf[0] = kfrag(0);
-        kf[1] = kfrag(1);
-        uint32_t pw[16];
-        float psum = l_run;
-        const bf16x2_t one = {(__bf16)1.0f, (__bf16)1.0f};
+    auto step = [&](f32x16_t (*sc)[2], f32x16_t (*sn)[2], int t) {
+        constexpr int NX = 2 * NKK;          // K fragments of S(t+1), each used by QG MFMAs
+        constexpr int WPM = 16 / NX;         // P words (2 weights) per group per fragment
+        constexpr int NY = NDB * FA_BC / 16; // V^T fragments of P V, each used by QG MFMAs
+        constexpr int MPM = 32 / (NY / 2);   // scores per group per fragment in the row max
+        constexpr int SPM = 16 / (NY / 2);   // P words per group per fragment in the row sum
+        const int k1 = (t + 1) % 3;
+        const uint16_t* kt = lds + k1 * S::KS;                          // K(t+1)
+        const uint16_t* kn = lds + (k1 == 2 ? 0 : k1 + 1) * S::KS;      // K(t+2)
+        uint16_t* kw = lds + (k1 == 0 ? 2 : k1 - 1) * S::KS;            // K(t+3), where K(t) was
+        const uint16_t* vt = lds + 3 * S::KS + (t & 1) * S::VS;         // V(t)
+        uint16_t* vw = lds + 3 * S::KS + ((t + 1) & 1) * S::VS;         // V(t+1)
+        // ---- X: S(t+1) = K(t+1) Q^T - m  ||  P(t) = 2^(S(t) - m)
+        bf16x8_t vf[3];
+        uint32_t pw[QG][16];
 #pragma unroll
         for (int i = 0; i < NX; ++i) {
-            if (i + 2 < NX) kf[(i + 2) % 3] = kfrag(i + 2);
+            if (i + 2 < NX) kf[(i + 2) % 3] = kfrag(kt, i + 2);
             const int kb2 = i / NKK, kk = i % NKK;
-            sn[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i % 3], qf[kk],
-                                                              kk == 0 ? negm : sn[kb2], 0, 0, 0);
+#pragma unroll
+            for (int qg = 0; qg < QG; ++qg) {
+                sn[qg][kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                    kf[i % 3], qf[qg][kk], kk == 0 ? negm[qg] : sn[qg][kb2], 0, 0, 0);
+#pragma unroll
+                for (int e = 0; e < WPM; ++e) {
+                    const int w = i * WPM + e;   // weights 2w, 2w+1 of the group's 32 scores
+                    const float p0 = fast_exp2(sc[qg][(2 * w) >> 4][(2 * w) & 15]);
+                    const float p1 = fast_exp2(sc[qg][(2 * w + 1) >> 4][(2 * w + 1) & 15]);
+                    pw[qg][w] = pack_bf16x2(p0, p1);
+                }
+                if (qg == QG - 1 && i + 2 == NX) vf[0] = vfrag(vt, 0);
+                if (qg == QG - 1 && i + 1 == NX) vf[1] = vfrag(vt, 1);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        bf16x8_t pb[QG][FA_BC / 16];
+#pragma unroll
+        for (int qg = 0; qg < QG; ++qg)
+#pragma unroll
+            for (int kk = 0; kk < FA_BC / 16; ++kk)
+                pb[qg][kk] = __builtin_bit_cast(bf16x8_t, u32x4_t{pw[qg][4 * kk], pw[qg][4 * kk + 1],
+                                                                  pw[qg][4 * kk + 2], pw[qg][4 * kk + 3]});
+        // ---- Y: O += V(t)^T P(t)  ||  row sum of P(t); K(t+3), V(t+1) into
+        // LDS; loads of K(t+4), V(t+2); row max of S(t+1); first K(t+2) fragments
+        const bf16x2_t one = {(__bf16)1.0f, (__bf16)1.0f};
+        float mx[QG], psum[QG];
+#pragma unroll
+        for (int qg = 0; qg < QG; ++qg) {
+            mx[qg] = -__builtin_inff();
+            psum[qg] = l_run[qg];
+        }
+#pragma unroll
+        for (int i = 0; i < NY; ++i) {
+            if (i + 2 < NY) vf[(i + 2) % 3] = vfrag(vt, i + 2);
+            if (i + 2 == NY) kf[0] = kfrag(kn, 0);
+            if (i + 1 == NY) kf[1] = kfrag(kn, 1);
+#pragma unroll
+            for (int qg = 0; qg < QG; ++qg) {
+                acc[qg][i / 4] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i % 3], pb[qg][i % 4],
+                                                                         acc[qg][i / 4], 0, 0, 0);
+                if (qg == 0) {
+                    if (i < S::KCH) store_k_chunk(kw, i);
+                    else if (i < S::KCH + 4) store_v_row(vw, i - S::KCH);
+                    else if (i == S::KCH + 4) load_k(t + 4);
+                    else if (i == S::KCH + 5) load_v(t + 2);
+                }
+                if (i < NY / 2) {
+#pragma unroll
+                    for (int e = 0; e < SPM; ++e) {
+                        const int w = i * SPM + e;
+                        psum[qg] = __builtin_amdgcn_fdot2_f32_bf16(
+                            __builtin_bit_cast(bf16x2_t, pw[qg][w]), one, psum[qg], false);
+                    }
+                    __asm__ volatile("" ::"v"(psum[qg]));   // keep the row sum in this group
+                } else {
+#pragma unroll
+                    for (int e = 0; e < MPM; ++e) {
+                        const int j = (i - NY / 2) * MPM + e;
+                        mx[qg] = fmaxf(mx[qg], sn[qg][j >> 4][j & 15]);
+                    }
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        bool need = false;
+#pragma unroll
+        for (int qg = 0; qg < QG; ++qg) {
+            l_run[qg] = psum[qg];
+            mx_next[qg] = half_max(mx[qg]);
+            need = need || mx_next[qg] > FA_LAZY_LOG2;
+        }
+        __syncthreads();
+        // ---- the last real tile: keys past the end take no weight
+        if (t + 1 == nt - 1 && tail) {
+            need = false;
+#pragma unroll
+            for (int qg = 0; qg < QG; ++qg) {
+                mask_tail(sn[qg], t + 1);
+                mx_next[qg] = row_max(sn[qg]);
+                need = need || mx_next[qg] > FA_LAZY_LOG2;
+            }
+        }
+        // ---- lazy rescale for S(t+1) (rare after the first tiles)
+        if (t + 1 < nt && __builtin_amdgcn_ballot_w64(need) != 0) {
+#pragma unroll
+            for (int qg = 0; qg < QG; ++qg) {
+                const float delta = fmaxf(mx_next[qg], 0.f);
+                const float alpha = fast_exp2(-delta);
+                m_ref[qg] += delta;
+                l_run[qg] *= alpha;
+#pragma unroll
+                for (int i = 0; i < NDB; ++i) acc[qg][i] *= alpha;
+                // -m is rewritten in place: a plain assignment here makes
+                // the register allocator copy the block on every tile.
+                const float nm = -m_ref[qg];
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    __asm__ volatile("v_mov_b32 %0, %1" : "+v"(negm[qg][i]) : "v"(nm));
+                    sn[qg][0][i] -= delta;
+                    sn[qg][1][i] -= delta;
+                }
+            }
+        }
+    };
+
+    for (int t = 0; t < nt; t += 2) {
+        step(sA, sB, t);
+        if (t + 1 >= nt) break;
+        step(sB, sA, t + 1);
+    }
+
+    // epilogue: combine the two halves' row sums, normalise, store
+#pragma unroll
+    for (int qg = 0; qg < QG; ++qg) {
+        const float l_tot = half_sum(l_run[qg]);
+        const float inv = 1.0f / l_tot;
+        if (qi[qg] < n) {
+            uint16_t* ob = a.o + off + qi[qg] * a.row_stride;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const f32x16_t& c = acc[qg][db];
+                    uint2 w;
+                    w.x = pack_bf16x2(c[4 * r + 0] * inv, c[4 * r + 1] * inv);
+                    w.y = pack_bf16x2(c[4 * r + 2] * inv, c[4 * r + 3] * inv);
+                    *(uint2*)(ob + db * 32 + 8 * r + 4 * g) = w;
+                }
+            if (a.lse != nullptr && g == 0)
+                a.lse[bh * n + qi[qg]] = (m_ref[qg] + __builtin_log2f(l_tot)) * 0.69314718055994531f;
+        }
+    }
+}
+
+// ---------------------------------------------------------------- bf16 MFMA, DMA staging
+//
+// Same computation and software pipeline as fa_fwd_bf16_kernel, for
+// head_dim 128, 8 waves and 256 query rows per workgroup, but the K and V
+// tiles go from global memory straight into LDS (buffer_load_dwordx4 ...
+// lds: one wave instruction moves 1 KiB, four 256-byte rows), so no VGPR
+// staging, no LDS store instructions and no register transpose.  Both tiles
+// are kept row-major in LDS, three buffers each, with the 16-byte chunks of
+// row r permuted by c -> c ^ dswz(r) (chosen by which global chunk each lane
+// fetches).  K fragments are plain 16-byte reads; V^T fragments for the
+// P V product come from ds_read_b64_tr_b16, which transposes 4 keys x 16
+// head-dim columns across each 16-lane group: source lane s reads 4
+// consecutive columns of key s / 4, and lane i receives column i of the 4
+// keys.
+
+// chunk permutation of a 256-byte row: a bijection on 0..15 (16 consecutive
+// rows hit 16 distinct chunks), and 4 consecutive rows differ in bits 2-3
+// (4 rows x 4 aligned chunks hit 16 distinct chunks)
+__device__ __forceinline__ int dswz(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
+
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+
+__device__ __forceinline__ bf16x4_t lds_read_tr(const lds_u8* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4_t*)p);
+}
+
+constexpr int FAD_WAVES = 8;
+
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * FAD_WAVES, 64 * FAD_WAVES),
+                          amdgpu_waves_per_eu(2, 2)))
+void fa_fwd_bf16_dma_kernel(FaArgs a) {
+    constexpr int D = 128, NKK = D / 16, NDB = D / 32;
+    constexpr int BR = 32 * FAD_WAVES;                // query rows per workgroup
+    constexpr int ROWB = 2 * D;                       // bytes per K or V row (256)
+    constexpr int TILEB = FA_BC * ROWB;               // bytes per tile (16 KiB)
+    constexpr int NI = TILEB / 1024 / FAD_WAVES;      // DMA instructions per wave per tensor (2)
+    __shared__ __attribute__((aligned(1024))) uint8_t lds_raw[6 * TILEB];
+    lds_u8* const lds = (lds_u8*)lds_raw;             // K buffers 0-2, V buffers 3-5
+
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63, l32 = lane & 31, g = lane >> 5;
+
+    const int64_t tile = xcd_remap(blockIdx.x, a.total_tiles);
+    const int qt = (int)(tile % a.n_qtiles);
+    const int64_t bh = tile / a.n_qtiles;
+    const int h = (int)(bh % a.heads);
+    const int64_t b = bh / a.heads;
+    const int64_t off = b * a.batch_stride + (int64_t)h * D;
+    const uint16_t* kb = a.k + off;
+    const uint16_t* vb = a.v + off;
+    const int64_t n = a.n;
+    const int nt = (int)((n + FA_BC - 1) / FA_BC);
+
+    const int64_t qi = (int64_t)qt * BR + wave * 32 + l32;
+    bf16x8_t qf[NKK];
+    load_q_fragment<D>(a, a.q + off, qi, g, qf);
+
+    // ---- DMA: instruction m of this wave fills rows 4 I .. 4 I + 3 of the
+    // tile, I = wave * NI + m; lane L writes LDS bytes 16 L .. of that KiB,
+    // i.e. row 4 I + L / 16, chunk slot L % 16, which holds global chunk
+    // (L % 16) ^ dswz(row).
+    const int64_t row_bytes = a.row_stride * 2;
+    uint32_t goff[NI];
+#pragma unroll
+    for (int m = 0; m < NI; ++m) {
+        const int row = (wave * NI + m) * 4 + (lane >> 4);
+        goff[m] = (uint32_t)(row * row_bytes + (((lane & 15) ^ dswz(row)) << 4));
+    }
+    auto dma = [&](const uint16_t* base, int t, lds_u8* buf) {
+        const int64_t kv0 = (int64_t)t * FA_BC;
+        const __amdgpu_buffer_rsrc_t r = buffer_rsrc(base + kv0 * a.row_stride, (n - kv0) * row_bytes);
+#pragma unroll
+        for (int m = 0; m < NI; ++m)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                r, (__attribute__((address_space(3))) void*)(buf + (wave * NI + m) * 1024), 16, goff[m], 0, 0, 0);
+    };
+    auto kbuf = [&](int j) { return lds + j * TILEB; };
+    auto vbuf = [&](int j) { return lds + (3 + j) * TILEB; };
+    // Fragment reads use a per-lane register offset plus a compile-time
+    // immediate (buffer and fragment), kept below the 64 KiB immediate
+    // range: the V region's base is folded into the per-lane V offsets.
+
+    // K fragment (kb2, kk): row kb2 * 32 + l32, chunk 2 kk + g
+    uint32_t koff[NKK];
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) koff[kk] = l32 * ROWB + (((2 * kk + g) ^ dswz(l32)) << 4);
+    auto kfrag = [&](int jk, int i) {   // K buffer jk (compile-time), fragment i
+        return *(const bf16x8_t*)(lds + koff[i % NKK] + (jk * TILEB + (i / NKK) * 32 * ROWB));
+    };
+    // V^T fragment (db, kk), half r: keys kk*16 + 4 (2r + g) + s / 4 (the
+    // S^T accumulator's key order), columns db*32 + 16 hh + 4 (s & 3)..+3,
+    // with s = lane & 15, hh = (lane >> 4) & 1
+    uint32_t voff[2][NDB];
+    {
+        const int s_ = lane & 15, hh = (lane >> 4) & 1;
+#pragma unroll
+        for (int r = 0; r < 2; ++r)
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) {
+                const int row = 4 * (2 * r + g) + (s_ >> 2);
+                const int chunk = 4 * db + 2 * hh + ((s_ & 3) >> 1);
+                voff[r][db] = 3 * TILEB + row * ROWB + ((chunk ^ dswz(row)) << 4) + (s_ & 1) * 8;
+            }
+    }
+    auto vfrag = [&](int jv, int i) {   // V buffer jv (compile-time), fragment i
+        const int db = i / 4, kk = i % 4;
+        const bf16x4_t lo = lds_read_tr(lds + voff[0][db] + (jv * TILEB + kk * 16 * ROWB));
+        const bf16x4_t hi = lds_read_tr(lds + voff[1][db] + (jv * TILEB + kk * 16 * ROWB));
+        return bf16x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    };
+
+    auto mask_tail = [&](f32x16_t& s0, f32x16_t& s1, int t) {
+        const int64_t kv0 = (int64_t)t * FA_BC;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int64_t key = kv0 + 8 * (i >> 2) + 4 * g + (i & 3);
+            if (key >= n) s0[i] = -__builtin_inff();
+            if (key + 32 >= n) s1[i] = -__builtin_inff();
+        }
+    };
+    auto row_max = [&](const f32x16_t& s0, const f32x16_t& s1) {
+        float mx = fmaxf(s0[0], s1[0]);
+#pragma unroll
+        for (int i = 1; i < 16; ++i) mx = fmaxf(mx, fmaxf(s0[i], s1[i]));
+        return half_max(mx);
+    };
+
+    f32x16_t acc[NDB];
+#pragma unroll
+    for (int i = 0; i < NDB; ++i) acc[i] = f32x16_t{};
+    f32x16_t negm = f32x16_t{};   // -m in every slot: the C operand of the first k-step
+    float m_ref, l_run = 0.f, mx_next = 0.f;
+    const bool tail = (n % FA_BC) != 0;
+
+    // ---- prologue: K(0..2), V(0..1) into LDS; S(0); m from tile 0
+    // S tiles rotate through three register blocks: step t reads S(t) from
+    // (x, y) and writes S(t+1) to (z, x), since the first half of S(t) is
+    // consumed before the second half of S(t+1) is started.
+    f32x16_t s0, s1, s2;
+    dma(kb, 0, kbuf(0));
+    dma(kb, 1, kbuf(1));
+    dma(kb, 2, kbuf(2));
+    dma(vb, 0, vbuf(0));
+    dma(vb, 1, vbuf(1));
+    __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0): this wave's tiles have landed
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+        s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfrag(0, kk), qf[kk], kk == 0 ? negm : s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfrag(0, NKK + kk), qf[kk], kk == 0 ? negm : s1, 0, 0, 0);
+    }
+    __syncthreads();              // K buffer 0 is refilled in the first iteration
+    if (nt == 1 && tail) mask_tail(s0, s1, 0);
+    {
+        const float mx = row_max(s0, s1);
+        m_ref = mx;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            negm[i] = -mx;
+            s0[i] -= mx;
+            s1[i] -= mx;
+        }
+    }
+    bf16x8_t kf[3];
+    kf[0] = kfrag(1, 0);
+    kf[1] = kfrag(1, 1);
+
+    // Step t uses K buffers (t+1) % 3 (read), (t+2) % 3 (next tile's first
+    // fragments), t % 3 (DMA target) and V buffers t % 3 (read), (t+2) % 3
+    // (DMA target); the loop is unrolled three times so all are compile-time.
+    auto step = [&](auto tm, f32x16_t& sc0, f32x16_t& sc1, f32x16_t& sn0, f32x16_t& sn1, int t) {
+        constexpr int T3 = decltype(tm)::value;   // t % 3
+        constexpr int NX = 2 * NKK;          // K fragments (MFMAs) of S(t+1)
+        constexpr int WPM = 16 / NX;         // P words (2 weights) per MFMA
+        constexpr int NY = NDB * FA_BC / 16; // V^T fragments (MFMAs) of P V
+        constexpr int MPM = 32 / (NY / 2);   // scores per MFMA in the row max
+        constexpr int SPM = 16 / (NY / 2);   // P words per MFMA in the row sum
+        constexpr int j0 = T3, j1 = (T3 + 1) % 3, j2 = (T3 + 2) % 3;
+        // ---- X: S(t+1) = K(t+1) Q^T - m  ||  P(t) = 2^(S(t) - m)
+        bf16x8_t vf[3];
+        uint32_t pw[16];
+#pragma unroll
+        for (int i = 0; i < NX; ++i) {
+            if (i + 2 < NX) kf[(i + 2) % 3] = kfrag(j1, i + 2);
+            const int kb2 = i / NKK, kk = i % NKK;
+            f32x16_t& d = kb2 ? sn1 : sn0;
+            d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i % 3], qf[kk], kk == 0 ? negm : d, 0, 0, 0);
 #pragma unroll
             for (int e = 0; e < WPM; ++e) {
-                const int w = i * WPM + e;   // weights 2w, 2w+1: scores (2w) / 16, (2w) % 16
-                const float p0 = fast_exp2(sc[(2 * w) >> 4][(2 * w) & 15]);
-                const float p1 = fast_exp2(sc[(2 * w + 1) >> 4][(2 * w + 1) & 15]);
+                const int w = i * WPM + e;   // weights 2w, 2w+1: block (2w) / 16 of S(t)
+                const f32x16_t& src = (2 * w) < 16 ? sc0 : sc1;
+                const float p0 = fast_exp2(src[(2 * w) & 15]);
+                const float p1 = fast_exp2(src[(2 * w + 1) & 15]);
                 pw[w] = pack_bf16x2(p0, p1);
-                psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pw[w]), one,
-                                                       psum, false);
             }
-            if (i + 2 == NX) vf[0] = vfrag(0);
-            if (i + 1 == NX) vf[1] = vfrag(1);
-            __asm__ volatile("" ::"v"(psum));   // keep the row sum in this group
+            if (i == 0) dma(kb, t + 3, kbuf(j0));   // K(t+3) where K(t) was
+            if (i == 1) dma(vb, t + 2, vbuf(j2));   // V(t+2) where V(t-1) was
+            if (i + 2 == NX) vf[0] = vfrag(j0, 0);
+            if (i + 1 == NX) vf[1] = vfrag(j0, 1);
             __builtin_amdgcn_sched_barrier(0);
         }
-        l_run = psum;
         bf16x8_t pb[FA_BC / 16];
 #pragma unroll
         for (int kk = 0; kk < FA_BC / 16; ++kk)
-            pb[kk] = __builtin_bit_cast(bf16x8_t, u32x4_t{pw[4 * kk], pw[4 * kk + 1],
-                                                          pw[4 * kk + 2], pw[4 * kk + 3]});
-        // ---- Y: O += V(t)^T P(t)  ||  K(t+2), V(t+1) into LDS; loads of
-        // K(t+3), V(t+2); row max of S(t+1)
-        float mx = -__builtin_inff();
+            pb[kk] = __builtin_bit_cast(bf16x8_t, u32x4_t{pw[4 * kk], pw[4 * kk + 1], pw[4 * kk + 2], pw[4 * kk + 3]});
+        // ---- Y: O += V(t)^T P(t)  ||  row sum of P(t); row max of S(t+1);
+        // first K(t+2) fragments
+        const bf16x2_t one = {(__bf16)1.0f, (__bf16)1.0f};
+        float mx = -__builtin_inff(), psum = l_run;
 #pragma unroll
         for (int i = 0; i < NY; ++i) {
-            if (i + 2 < NY) vf[(i + 2) % 3] = vfrag(i + 2);
-            acc[i / 4] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i % 3], pb[i % 4], acc[i / 4],
-                                                                 0, 0, 0);
-            if (i < S::KCH) store_k_chunk(kbuf[P], i);
-            else if (i < S::KCH + 4) store_v_row(vbuf[P ^ 1], i - S::KCH);
-            else if (i == S::KCH + 4) load_k(t + 3);
-            else if (i == S::KCH + 5) load_v(t + 2);
-            if (i >= NY / 2) {
+            if (i + 2 < NY) vf[(i + 2) % 3] = vfrag(j0, i + 2);
+            acc[i / 4] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i % 3], pb[i % 4], acc[i / 4], 0, 0, 0);
+            if (i < NY / 2) {
+#pragma unroll
+                for (int e = 0; e < SPM; ++e)
+                    psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pw[i * SPM + e]),
+                                                           one, psum, false);
+                __asm__ volatile("" ::"v"(psum));   // keep the row sum in this group
+            } else {
 #pragma unroll
                 for (int e = 0; e < MPM; ++e) {
                     const int j = (i - NY / 2) * MPM + e;
-                    mx = fmaxf(mx, sn[j >> 4][j & 15]);
+                    mx = fmaxf(mx, (j < 16 ? sn0 : sn1)[j & 15]);
                 }
             }
             __builtin_amdgcn_sched_barrier(0);
         }
+        l_run = psum;
         mx_next = half_max(mx);
+        // The tiles DMA'd in the previous iteration (K(t+2), V(t+1)) are
+        // read after this barrier; this iteration's 2 NI requests may stay
+        // in flight.  vmcnt counts only these DMAs in the loop.
+        __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * NI));
         __syncthreads();
+        kf[0] = kfrag(j2, 0);
+        kf[1] = kfrag(j2, 1);
         // ---- the last real tile: keys past the end take no weight
         if (t + 1 == nt - 1 && tail) {
-            mask_tail(sn, t + 1);
-            mx_next = row_max(sn);
+            mask_tail(sn0, sn1, t + 1);
+            mx_next = row_max(sn0, sn1);
         }
         // ---- lazy rescale for S(t+1) (rare after the first tiles)
         if (t + 1 < nt && __builtin_amdgcn_ballot_w64(mx_next > FA_LAZY_LOG2) != 0) {
@@ -433,19 +791,21 @@ void fa_fwd_bf16_kernel(FaArgs a) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 __asm__ volatile("v_mov_b32 %0, %1" : "+v"(negm[i]) : "v"(nm));
-                sn[0][i] -= delta;
-                sn[1][i] -= delta;
+                sn0[i] -= delta;
+                sn1[i] -= delta;
             }
         }
     };
 
-    for (int t = 0; t < nt; t += 2) {
-        step(std::integral_constant<int, 0>{}, sA, sB, t);
+    for (int t = 0; t < nt; t += 3) {
+        step(std::integral_constant<int, 0>{}, s0, s1, s2, s0, t);
         if (t + 1 >= nt) break;
-        step(std::integral_constant<int, 1>{}, sB, sA, t + 1);
+        step(std::integral_constant<int, 1>{}, s2, s0, s1, s2, t + 1);
+        if (t + 2 >= nt) break;
+        step(std::integral_constant<int, 2>{}, s1, s2, s0, s1, t + 2);
     }
+    __builtin_amdgcn_s_waitcnt(0x0070);   // no DMA may land after the workgroup's LDS is released
 
-    // epilogue: combine the two halves' row sums, normalise, store
     const float l_tot = half_sum(l_run);
     const float inv = 1.0f / l_tot;
     if (qi < n) {
@@ -559,6 +919,12 @@ void fa_fwd_f32_kernel(FaArgs a) {
 
 // ---------------------------------------------------------------- launch
 
+// Query rows one workgroup covers (the host sizes the grid with it).
+int flash_attn_rows_per_workgroup(bool bf16, int64_t head_dim) {
+    if (bf16 && head_dim == 128 && VX_FA_DMA) return 32 * FAD_WAVES;
+    return bf16 ? 32 * FA_QG * FA_WAVES : 256 / (int)(head_dim / 32);
+}
+
 hipError_t launch_flash_attn(const void* q, const void* k, const void* v, void* o, float* lse,
                              int64_t batch, int64_t n, int64_t heads, int64_t head_dim,
                              float scale, const RopeArgs* rope, bool bf16, hipStream_t st) {
@@ -578,14 +944,16 @@ hipError_t launch_flash_attn(const void* q, const void* k, const void* v, void* 
     if (rope) a.rope = *rope;
     else a.rope = RopeArgs{1, 1, 1, 0, 0, 0, 0, 1.f};
 
-    const int rows_per_wg = bf16 ? 32 * FA_WAVES : 256 / (int)(head_dim / 32);
+    const int rows_per_wg = flash_attn_rows_per_workgroup(bf16, head_dim);
     a.n_qtiles = (int)((n + rows_per_wg - 1) / rows_per_wg);
     a.total_tiles = batch * heads * a.n_qtiles;
     const dim3 grid((unsigned)a.total_tiles);
     if (bf16) {
         const dim3 block(64 * FA_WAVES);
-        if (head_dim == 128) hipLaunchKernelGGL((fa_fwd_bf16_kernel<128, FA_WAVES>), grid, block, 0, st, a);
-        else hipLaunchKernelGGL((fa_fwd_bf16_kernel<64, FA_WAVES>), grid, block, 0, st, a);
+        if (head_dim == 128 && VX_FA_DMA)
+            hipLaunchKernelGGL(fa_fwd_bf16_dma_kernel, grid, dim3(64 * FAD_WAVES), 0, st, a);
+        else if (head_dim == 128) hipLaunchKernelGGL((fa_fwd_bf16_kernel<128, FA_WAVES, FA_QG>), grid, block, 0, st, a);
+        else hipLaunchKernelGGL((fa_fwd_bf16_kernel<64, FA_WAVES, FA_QG>), grid, block, 0, st, a);
     } else {
         const dim3 block(256);
         if (head_dim == 128) hipLaunchKernelGGL(fa_fwd_f32_kernel<128>, grid, block, 0, st, a);
@@ -594,9 +962,5 @@ hipError_t launch_flash_attn(const void* q, const void* k, const void* v, void* 
     return hipGetLastError();
 }
 
-// Query rows one bf16 workgroup covers (the host sizes the grid with it).
-int flash_attn_rows_per_workgroup(bool bf16, int64_t head_dim) {
-    return bf16 ? 32 * FA_WAVES : 256 / (int)(head_dim / 32);
-}
 
 }  // namespace vx
