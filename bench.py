@@ -43,11 +43,33 @@ def parse():
     p.add_argument("--workload", default="large")
     p.add_argument("--rope", choices=["fused", "separate"], default="fused",
                    help="fused: K rotated by vx_rope3d_apply, Q inside the attention load")
-    p.add_argument("--cpu-rows", type=int, default=192,
+    p.add_argument("--cpu-rows", type=int, default=512,
                    help="query rows of the oracle CPU baseline (0 = skip it)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run a plain 1 GiB elementwise copy (HBM counter calibration)")
     return p.parse_args()
+
+
+def attention_kernel_name(wl):
+    if wl.dtype != "bf16":
+        return f"fa_fwd_f32_kernel<{wl.head_dim}>"
+    return "fa_fwd_bf16_dma_kernel" if wl.head_dim == 128 else f"fa_fwd_bf16_kernel<{wl.head_dim}, 8, 1>"
+
+
+def measured_traffic(wl):
+    """HBM bytes per attention launch from the committed rocprofv3 FETCH_SIZE /
+    WRITE_SIZE record (scaled by the copy calibration), or None when the record
+    is for another workload or the kernel source has changed since."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "attention_large_traffic.json")
+    if wl.name != "large" or not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    with open(os.path.join(ROOT, rec["source"]), "rb") as f:
+        if hashlib.sha256(f.read()).hexdigest() != rec["source_sha256"]:
+            return None
+    return rec["bytes_per_launch"]
 
 
 def cpu_baseline(wl, q, k, v, rows_count):
@@ -194,8 +216,8 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
-            "traffic": None,
-            "kernel": "fa_fwd_bf16_kernel<128>",
+            "traffic": measured_traffic(wl),
+            "kernel": attention_kernel_name(wl),
         },
         "kernels": kernels,
         "device": {"name": props.name, "cus": props.multi_processor_count,
