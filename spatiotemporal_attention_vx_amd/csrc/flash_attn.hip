@@ -54,6 +54,12 @@
 #ifndef VX_FA_DMA
 #define VX_FA_DMA 1
 #endif
+#ifndef VX_FA_DMA_SPREAD
+#define VX_FA_DMA_SPREAD 1
+#endif
+#ifndef VX_FA_DMA_ASM
+#define VX_FA_DMA_ASM 1
+#endif
 
 namespace vx {
 
@@ -603,13 +609,30 @@ void fa_fwd_bf16_dma_kernel(FaArgs a) {
         const int row = (wave * NI + m) * 4 + (lane >> 4);
         goff[m] = (uint32_t)(row * row_bytes + (((lane & 15) ^ dswz(row)) << 4));
     }
-    auto dma = [&](const uint16_t* base, int t, lds_u8* buf) {
+    const int swave = __builtin_amdgcn_readfirstlane(wave);   // wave-uniform, for M0
+    // The DMA is written as inline assembly: with the builtin, the compiler
+    // cannot tell the destination from the buffers being read and waits for
+    // every DMA in flight (vmcnt(0)) before each V read.  Ordering is kept by
+    // hand instead: an explicit vmcnt wait and the barrier publish a tile,
+    // and no buffer is a DMA target while any wave may still read it.
+    auto dma_one = [&](const uint16_t* base, int t, lds_u8* buf, int m) {
         const int64_t kv0 = (int64_t)t * FA_BC;
         const __amdgpu_buffer_rsrc_t r = buffer_rsrc(base + kv0 * a.row_stride, (n - kv0) * row_bytes);
+        const uint32_t dst = (uint32_t)(uintptr_t)(buf + (swave * NI + m) * 1024);
+#if VX_FA_DMA_ASM
+        __asm__ volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                         :
+                         : "s"(dst), "v"(goff[m]), "s"(r)
+                         : "m0");
+#else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            r, (__attribute__((address_space(3))) void*)(buf + (swave * NI + m) * 1024), 16, goff[m], 0, 0, 0);
+        (void)dst;
+#endif
+    };
+    auto dma = [&](const uint16_t* base, int t, lds_u8* buf) {
 #pragma unroll
-        for (int m = 0; m < NI; ++m)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                r, (__attribute__((address_space(3))) void*)(buf + (wave * NI + m) * 1024), 16, goff[m], 0, 0, 0);
+        for (int m = 0; m < NI; ++m) dma_one(base, t, buf, m);
     };
     auto kbuf = [&](int j) { return lds + j * TILEB; };
     auto vbuf = [&](int j) { return lds + (3 + j) * TILEB; };
@@ -730,8 +753,13 @@ void fa_fwd_bf16_dma_kernel(FaArgs a) {
                 const float p1 = fast_exp2(src[(2 * w + 1) & 15]);
                 pw[w] = pack_bf16x2(p0, p1);
             }
+#if VX_FA_DMA_SPREAD
+            // K(t+3) where K(t) was, spread over the phase
+            if (i % (NX / NI) == 0) dma_one(kb, t + 3, kbuf(j0), i / (NX / NI));
+#else
             if (i == 0) dma(kb, t + 3, kbuf(j0));   // K(t+3) where K(t) was
             if (i == 1) dma(vb, t + 2, vbuf(j2));   // V(t+2) where V(t-1) was
+#endif
             if (i + 2 == NX) vf[0] = vfrag(j0, 0);
             if (i + 1 == NX) vf[1] = vfrag(j0, 1);
             __builtin_amdgcn_sched_barrier(0);
@@ -748,6 +776,10 @@ void fa_fwd_bf16_dma_kernel(FaArgs a) {
         for (int i = 0; i < NY; ++i) {
             if (i + 2 < NY) vf[(i + 2) % 3] = vfrag(j0, i + 2);
             acc[i / 4] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i % 3], pb[i % 4], acc[i / 4], 0, 0, 0);
+#if VX_FA_DMA_SPREAD
+            // V(t+2) where V(t-1) was, spread over the phase
+            if (i % (NY / NI) == 0) dma_one(vb, t + 2, vbuf(j2), i / (NY / NI));
+#endif
             if (i < NY / 2) {
 #pragma unroll
                 for (int e = 0; e < SPM; ++e)
