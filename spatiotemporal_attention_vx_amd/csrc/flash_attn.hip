@@ -8,8 +8,8 @@
 // attention, Dao et al. 2022: an online softmax over key tiles, so the
 // N x N score matrix never exists).
 //
-// bf16 path (the hot one).  A workgroup of WAVES waves owns 32 * WAVES
-// query rows of one (batch, head); each wave owns 32 rows.
+// bf16 path (the hot one).  A workgroup of 8 waves owns 256 query rows of
+// one (batch, head); each wave owns 32 rows.
 //   * Scores are formed transposed, S^T (32 keys x 32 queries) = K_tile Q^T,
 //     with v_mfma_f32_32x32x16_bf16: K rows come from LDS as the A operand,
 //     the wave's Q^T fragment stays in VGPRs as the B operand.  In the
@@ -25,15 +25,24 @@
 //     was actually subtracted, so the result is exact up to rounding.
 //   * P^T is rounded to bf16 in registers and is directly the B operand of
 //     O^T (d x 32 queries) += V^T P^T; the k index of that product runs
-//     over keys in the order the S^T accumulator hands them out, and V^T is
-//     stored in LDS in that key order, so no shuffle is needed.  The row
-//     sum is taken over the same rounded weights with v_dot2_f32_bf16.
+//     over keys in the order the S^T accumulator hands them out, and the
+//     V^T fragments are read in that key order, so P never touches LDS.  The
+//     row sum is taken over the same rounded weights with v_dot2_f32_bf16.
 //   * Software pipeline, one key tile t per iteration:
-//       X: S(t+1) = K(t+1) Q^T (MFMA)  interleaved with  exp/convert/sum of S(t)
-//       Y: O += V(t)^T P(t)   (MFMA)  interleaved with  row max of S(t+1),
-//          LDS stores of K(t+2) and V(t+1), global loads of K(t+3), V(t+2)
-//     K and V^T tiles are double-buffered in LDS with one barrier per tile.
-//     Tiles past the sequence end are read through a buffer resource that
+//       X: S(t+1) = K(t+1) Q^T (MFMA)  interleaved with  exp/convert of S(t)
+//       Y: O += V(t)^T P(t)   (MFMA)  interleaved with  row sum of P(t),
+//          row max of S(t+1)
+//     with the tile loads for later iterations spread over both phases and
+//     one barrier per tile.  Each MFMA and the work meant to run under it
+//     form a group that sched_barrier(0) keeps in order.
+//   * head_dim 128 (fa_fwd_bf16_dma_kernel): K and V tiles go from global
+//     memory straight into LDS (buffer_load_dwordx4 ... lds), row-major with
+//     a per-row 16-byte chunk permutation, three buffers each; V^T fragments
+//     come from the transposing LDS read ds_read_b64_tr_b16.
+//     head_dim 64 (fa_fwd_bf16_kernel): K and V tiles are staged through
+//     VGPRs; V is transposed in registers and stored as V^T with an XOR
+//     chunk permutation, K with padded rows.
+//   * Tiles past the sequence end are read through a buffer resource that
 //     ends at the sequence end, so they load as zeros with no per-lane test;
 //     scores of keys past the end are set to -inf in the last real tile.
 //   * Workgroups are remapped so each XCD works through a contiguous range
@@ -51,15 +60,7 @@
 #ifndef VX_FA_QG
 #define VX_FA_QG 1
 #endif
-#ifndef VX_FA_DMA
-#define VX_FA_DMA 1
-#endif
-#ifndef VX_FA_DMA_SPREAD
-#define VX_FA_DMA_SPREAD 1
-#endif
-#ifndef VX_FA_DMA_ASM
-#define VX_FA_DMA_ASM 1
-#endif
+
 
 namespace vx {
 
@@ -619,16 +620,10 @@ void fa_fwd_bf16_dma_kernel(FaArgs a) {
         const int64_t kv0 = (int64_t)t * FA_BC;
         const __amdgpu_buffer_rsrc_t r = buffer_rsrc(base + kv0 * a.row_stride, (n - kv0) * row_bytes);
         const uint32_t dst = (uint32_t)(uintptr_t)(buf + (swave * NI + m) * 1024);
-#if VX_FA_DMA_ASM
         __asm__ volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                          :
                          : "s"(dst), "v"(goff[m]), "s"(r)
                          : "m0");
-#else
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            r, (__attribute__((address_space(3))) void*)(buf + (swave * NI + m) * 1024), 16, goff[m], 0, 0, 0);
-        (void)dst;
-#endif
     };
     auto dma = [&](const uint16_t* base, int t, lds_u8* buf) {
 #pragma unroll
@@ -753,13 +748,8 @@ void fa_fwd_bf16_dma_kernel(FaArgs a) {
                 const float p1 = fast_exp2(src[(2 * w + 1) & 15]);
                 pw[w] = pack_bf16x2(p0, p1);
             }
-#if VX_FA_DMA_SPREAD
-            // K(t+3) where K(t) was, spread over the phase
+            // K(t+3) where K(t) was, one request every NX / NI groups
             if (i % (NX / NI) == 0) dma_one(kb, t + 3, kbuf(j0), i / (NX / NI));
-#else
-            if (i == 0) dma(kb, t + 3, kbuf(j0));   // K(t+3) where K(t) was
-            if (i == 1) dma(vb, t + 2, vbuf(j2));   // V(t+2) where V(t-1) was
-#endif
             if (i + 2 == NX) vf[0] = vfrag(j0, 0);
             if (i + 1 == NX) vf[1] = vfrag(j0, 1);
             __builtin_amdgcn_sched_barrier(0);
@@ -776,10 +766,8 @@ void fa_fwd_bf16_dma_kernel(FaArgs a) {
         for (int i = 0; i < NY; ++i) {
             if (i + 2 < NY) vf[(i + 2) % 3] = vfrag(j0, i + 2);
             acc[i / 4] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i % 3], pb[i % 4], acc[i / 4], 0, 0, 0);
-#if VX_FA_DMA_SPREAD
-            // V(t+2) where V(t-1) was, spread over the phase
+            // V(t+2) where V(t-1) was, one request every NY / NI groups
             if (i % (NY / NI) == 0) dma_one(vb, t + 2, vbuf(j2), i / (NY / NI));
-#endif
             if (i < NY / 2) {
 #pragma unroll
                 for (int e = 0; e < SPM; ++e)
@@ -953,7 +941,7 @@ void fa_fwd_f32_kernel(FaArgs a) {
 
 // Query rows one workgroup covers (the host sizes the grid with it).
 int flash_attn_rows_per_workgroup(bool bf16, int64_t head_dim) {
-    if (bf16 && head_dim == 128 && VX_FA_DMA) return 32 * FAD_WAVES;
+    if (bf16 && head_dim == 128) return 32 * FAD_WAVES;
     return bf16 ? 32 * FA_QG * FA_WAVES : 256 / (int)(head_dim / 32);
 }
 
@@ -982,9 +970,7 @@ hipError_t launch_flash_attn(const void* q, const void* k, const void* v, void* 
     const dim3 grid((unsigned)a.total_tiles);
     if (bf16) {
         const dim3 block(64 * FA_WAVES);
-        if (head_dim == 128 && VX_FA_DMA)
-            hipLaunchKernelGGL(fa_fwd_bf16_dma_kernel, grid, dim3(64 * FAD_WAVES), 0, st, a);
-        else if (head_dim == 128) hipLaunchKernelGGL((fa_fwd_bf16_kernel<128, FA_WAVES, FA_QG>), grid, block, 0, st, a);
+        if (head_dim == 128) hipLaunchKernelGGL(fa_fwd_bf16_dma_kernel, grid, dim3(64 * FAD_WAVES), 0, st, a);
         else hipLaunchKernelGGL((fa_fwd_bf16_kernel<64, FA_WAVES, FA_QG>), grid, block, 0, st, a);
     } else {
         const dim3 block(256);
