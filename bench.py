@@ -112,7 +112,7 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     binding.load()
-    wl = configs.WORKLOADS[args.workload]
+    wl = configs.get(args.workload)
     dev = torch.device("cuda:0")
     props = torch.cuda.get_device_properties(dev)
 
@@ -189,7 +189,9 @@ def main():
         "rope_hbm_frac": round(rope_bytes / (ms["rope"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
     }
     record = {
-        "metric": METRIC,
+        "metric": METRIC if wl.name == configs.BENCH_WORKLOAD else
+        (f"flash-attn TFLOP/s + % bf16 MFMA peak at {wl.n_tokens:,} tokens, "
+         f"{wl.heads} heads × d{wl.head_dim}"),
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -208,7 +210,10 @@ def main():
                          f"{wl.dtype}, batch {wl.batch}"),
             "tokens": wl.n_tokens, "heads": wl.heads, "head_dim": wl.head_dim,
             "batch": wl.batch, "rope": args.rope,
-            "step": "adaln [N, H*d] + rope3d + flash attention fwd",
+            "step": (f"adaln [{wl.adaln_rows}, {wl.adaln_hidden}] + rope3d + flash attention fwd"
+                     + (f"; one GPU's share of sequence parallelism over {wl.sp} GPUs "
+                        f"(token shard for adaln, {wl.heads} of {wl.sp * wl.heads} heads "
+                        f"for attention; all-to-alls not included)" if wl.sp > 1 else "")),
         },
         "roofline": {
             "bound": "mfma",

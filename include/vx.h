@@ -6,6 +6,10 @@
  *   vx_adaln_modulate   per-token AdaLN modulation
  *   vx_rope3d_apply     3D rotary position embedding on Q and K
  *   vx_flash_attn_fwd   full non-causal attention, flash style
+ * and, for attention whose keys are split into parts (sharded or in
+ * passes):
+ *   vx_flash_attn_fwd_kv  attention of one token set over another
+ *   vx_attn_merge2        two partial results combined through their LSEs
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -125,6 +129,49 @@ int vx_flash_attn_fwd(const void* q, const void* k, const void* v, void* o, floa
                       int64_t batch, int64_t n_tokens, int64_t heads, int64_t head_dim,
                       float softmax_scale, const vx_rope3d_desc* rope_q, int dt,
                       void* hip_stream);
+
+/*
+ * Attention of n_q queries over a separate set of n_kv keys (and values):
+ * the same definition as vx_flash_attn_fwd with the sum over j running over
+ * the n_kv keys.  This is the building block of attention whose keys are
+ * split into parts, by a key-sharded sequence (vidax paper §2
+ * "Spatiotemporal tensor and sequence sharding": the token axis is cut
+ * across devices) or by passes over a long sequence; the parts are then
+ * combined with vx_attn_merge2 through their LSEs.
+ *
+ * q, o: [batch, n_q, heads, head_dim]; k, v: [batch, n_kv, heads, head_dim],
+ * all of type dt; lse: float32 [batch, heads, n_q] or NULL.  rope_q, if
+ * non-NULL, describes the n_q query tokens (T*H*W + n_prefix == n_q).
+ * vx_flash_attn_fwd(..., n_tokens, ...) is this call with n_q = n_kv =
+ * n_tokens.  Errors: as vx_flash_attn_fwd, with n_q <= 0 or n_kv <= 0
+ * reported as VX_ERR_INVALID.
+ */
+int vx_flash_attn_fwd_kv(const void* q, const void* k, const void* v, void* o, float* lse,
+                         int64_t batch, int64_t n_q, int64_t n_kv, int64_t heads,
+                         int64_t head_dim, float softmax_scale, const vx_rope3d_desc* rope_q,
+                         int dt, void* hip_stream);
+
+/*
+ * Merge of two partial attention results over disjoint key sets A and B
+ * into the result over A u B (the consumer of the LSE output; same source
+ * as vx_flash_attn_fwd_kv):
+ *
+ *   lse = log(exp(lse_a) + exp(lse_b))
+ *   o   = exp(lse_a - lse) * o_a + exp(lse_b - lse) * o_b
+ *
+ * per (batch, token, head).  o_a, o_b, o: [batch, n_tokens, heads, head_dim]
+ * of type dt; lse_a, lse_b: float32 [batch, heads, n_tokens]; lse: the same,
+ * or NULL (not written).  Both LSEs -inf (two empty parts) gives o = 0 and
+ * lse = -inf.  In place is allowed: o may be exactly o_a or o_b, lse exactly
+ * lse_a or lse_b; any other overlap is invalid.  P parts merge pairwise (the
+ * operation is associative up to rounding).
+ * Errors: VX_ERR_NULL (o_a, lse_a, o_b, lse_b or o NULL); VX_ERR_INVALID
+ * (sizes <= 0, bad dt, overlaps); VX_ERR_UNSUPPORTED (head_dim not 64 or
+ * 128); VX_ERR_ALIGN (o tensors not 16-byte, LSEs not 4-byte aligned).
+ */
+int vx_attn_merge2(const void* o_a, const float* lse_a, const void* o_b, const float* lse_b,
+                   void* o, float* lse, int64_t batch, int64_t n_tokens, int64_t heads,
+                   int64_t head_dim, int dt, void* hip_stream);
 
 /* Message of the last failed vx_* call on this thread ("" if none). */
 const char* vx_last_error(void);

@@ -14,6 +14,16 @@ definition, materialising each score row in full:
     lse = max s + ln sum_j exp(s_j - max s)
 
 No mask, no causality, no dropout.  scale defaults to 1 / sqrt(head_dim).
+The queries and the keys may be different token sets (q has its own row
+count), which is attention over one part of a key-split sequence.
+
+``merge_lse`` combines two such partial results over disjoint key sets.
+From the definition, exp(lse) is a row's softmax denominator Z and o its
+Z-weighted mean of values, so over the union
+    Z = Z_a + Z_b,   o = (Z_a o_a + Z_b o_b) / Z,   lse = ln Z.
+This is the step that puts a key-sharded attention back together (the
+vidax paper §2 "Spatiotemporal tensor and sequence sharding" shards the
+token axis across devices).
 """
 from __future__ import annotations
 
@@ -53,6 +63,29 @@ def attention(q, k, v, scale: float = 0.0, rows=None, row_block: int = 512):
             total = e.sum(axis=1, keepdims=True)
             o[r0:r0 + sel.size, h, :] = (e @ vh) / total
             lse[h, r0:r0 + sel.size] = m[:, 0] + np.log(total[:, 0])
+    return o, lse
+
+
+def merge_lse(o_a, lse_a, o_b, lse_b):
+    """Attention over two disjoint key sets from their partial results.
+
+    o_a, o_b: [R, H, d]; lse_a, lse_b: [H, R] (as ``attention`` returns
+    them).  Returns (o [R, H, d], lse [H, R]) in float64.  A part with
+    lse = -inf (no keys) has Z = 0; two such parts give o = 0, lse = -inf.
+    """
+    o_a, o_b = np.asarray(o_a, np.float64), np.asarray(o_b, np.float64)
+    lse_a, lse_b = np.asarray(lse_a, np.float64), np.asarray(lse_b, np.float64)
+    m = np.maximum(lse_a, lse_b)
+    empty = np.isneginf(m)
+    m_safe = np.where(empty, 0.0, m)
+    z_a = np.exp(lse_a - m_safe)           # Z_a / e^m  (0 for an empty part)
+    z_b = np.exp(lse_b - m_safe)
+    z = z_a + z_b
+    z_safe = np.where(empty, 1.0, z)
+    w_a = (z_a / z_safe).T[:, :, None]     # [R, H, 1]
+    w_b = (z_b / z_safe).T[:, :, None]
+    o = w_a * o_a + w_b * o_b
+    lse = np.where(empty, -np.inf, m_safe + np.log(z_safe))
     return o, lse
 
 

@@ -16,8 +16,8 @@ from . import build as _build
 VX_F32, VX_BF16 = 0, 1
 STATUS = {0: "VX_OK", 1: "VX_ERR_NULL", 2: "VX_ERR_INVALID", 3: "VX_ERR_UNSUPPORTED",
           4: "VX_ERR_ALIGN", 5: "VX_ERR_HIP"}
-EXPORTS = ("vx_adaln_modulate", "vx_rope3d_apply", "vx_flash_attn_fwd", "vx_last_error",
-           "vx_version")
+EXPORTS = ("vx_adaln_modulate", "vx_rope3d_apply", "vx_flash_attn_fwd", "vx_flash_attn_fwd_kv",
+           "vx_attn_merge2", "vx_last_error", "vx_version")
 
 
 class VxError(RuntimeError):
@@ -59,6 +59,11 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.vx_flash_attn_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_float,
                                       ctypes.POINTER(RopeDesc), ctypes.c_int, vp]
     lib.vx_flash_attn_fwd.restype = ctypes.c_int
+    lib.vx_flash_attn_fwd_kv.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
+                                         ctypes.c_float, ctypes.POINTER(RopeDesc), ctypes.c_int, vp]
+    lib.vx_flash_attn_fwd_kv.restype = ctypes.c_int
+    lib.vx_attn_merge2.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_int, vp]
+    lib.vx_attn_merge2.restype = ctypes.c_int
     lib.vx_last_error.argtypes = []
     lib.vx_last_error.restype = ctypes.c_char_p
     lib.vx_version.argtypes = []
@@ -134,18 +139,54 @@ def rope3d_apply(q, k, rope: RopeDesc, stream=None):
                                   _dtype_code(ref), _stream(stream)))
 
 
+def _check_lse(lse, b, h, n, name="lse"):
+    if lse is None:
+        return
+    import torch
+    if (not lse.is_cuda or not lse.is_contiguous() or lse.dtype != torch.float32
+            or tuple(lse.shape) != (b, h, n)):
+        raise ValueError(f"{name} must be a contiguous float32 GPU tensor of shape {(b, h, n)}")
+
+
 def flash_attn_fwd(q, k, v, o, lse=None, softmax_scale: float = 0.0,
                    rope_q: RopeDesc | None = None, stream=None):
     """o = softmax(scale q k^T) v for [B, N, H, d] tensors; optional lse [B, H, N]."""
     _same(q, k, v, o, names=("q", "k", "v", "o"))
     b, n, h, d = q.shape
-    if lse is not None:
-        import torch
-        if (not lse.is_cuda or not lse.is_contiguous() or lse.dtype != torch.float32
-                or tuple(lse.shape) != (b, h, n)):
-            raise ValueError(f"lse must be a contiguous float32 GPU tensor of shape {(b, h, n)}")
+    _check_lse(lse, b, h, n)
     _check(load().vx_flash_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), b, n, h, d,
                                     softmax_scale,
                                     ctypes.byref(rope_q) if rope_q is not None else None,
                                     _dtype_code(q), _stream(stream)))
+    return o
+
+
+def flash_attn_fwd_kv(q, k, v, o, lse=None, softmax_scale: float = 0.0,
+                      rope_q: RopeDesc | None = None, stream=None):
+    """Attention of q, o [B, Nq, H, d] over k, v [B, Nkv, H, d]; optional lse [B, H, Nq]."""
+    _same(q, o, names=("q", "o"))
+    _same(k, v, names=("k", "v"))
+    b, nq, h, d = q.shape
+    if k.dtype != q.dtype or k.shape[0] != b or tuple(k.shape[2:]) != (h, d):
+        raise ValueError(f"k is {tuple(k.shape)} {k.dtype}, q is {tuple(q.shape)} {q.dtype}")
+    nk = k.shape[1]
+    _check_lse(lse, b, h, nq)
+    _check(load().vx_flash_attn_fwd_kv(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), b, nq, nk,
+                                       h, d, softmax_scale,
+                                       ctypes.byref(rope_q) if rope_q is not None else None,
+                                       _dtype_code(q), _stream(stream)))
+    return o
+
+
+def attn_merge2(o_a, lse_a, o_b, lse_b, o, lse=None, stream=None):
+    """Merge two partial attention results ([B, N, H, d] + lse [B, H, N]) by their LSEs."""
+    _same(o_a, o_b, o, names=("o_a", "o_b", "o"))
+    b, n, h, d = o_a.shape
+    for name, t in (("lse_a", lse_a), ("lse_b", lse_b)):
+        if t is None:
+            raise ValueError(f"{name} is required")
+        _check_lse(t, b, h, n, name)
+    _check_lse(lse, b, h, n)
+    _check(load().vx_attn_merge2(_ptr(o_a), _ptr(lse_a), _ptr(o_b), _ptr(lse_b), _ptr(o),
+                                 _ptr(lse), b, n, h, d, _dtype_code(o_a), _stream(stream)))
     return o

@@ -29,6 +29,17 @@ class Workload:
     eps: float = 1e-6       # LayerNorm epsilon
     batch: int = 1
     oracle_rows: int = 0    # 0: the oracle checks every row; else a sample
+    sp: int = 1             # sequence-parallel degree this is one GPU's share of
+
+    @property
+    def adaln_rows(self) -> int:
+        """Tokens one GPU modulates: its token shard, the largest of an even split."""
+        return -(-self.n_tokens // self.sp)
+
+    @property
+    def adaln_hidden(self) -> int:
+        """AdaLN row width: the model width, all heads (sp * heads * head_dim)."""
+        return self.sp * self.heads * self.head_dim
 
     @property
     def n_video(self) -> int:
@@ -53,7 +64,7 @@ class Workload:
 
     def adaln_bytes(self) -> float:
         """x, shift, scale read once and y written once."""
-        return 4.0 * self.n_tokens * self.hidden * self.elem_bytes() * self.batch
+        return 4.0 * self.adaln_rows * self.adaln_hidden * self.elem_bytes() * self.batch
 
     def rope_bytes(self) -> float:
         """Rotated rows of Q and K read and written once."""
@@ -70,6 +81,38 @@ WORKLOADS = {
     "mixed": Workload("mixed", 4, (21, 48, 85), 226, 48, 64, "bf16", (16, 24, 24),
                       oracle_rows=256),
 }
+
+# One GPU's share of a workload under Ulysses sequence parallelism over P
+# GPUs (vidax paper §2 "Spatiotemporal tensor and sequence sharding": tokens
+# are sharded for the per-token work, an all-to-all regathers the sequence
+# and shards the heads for attention; §3.1 Table 1 runs Wan2.2 A14B with
+# SP 2 and CogVideoX1.5 with SP 4).  A GPU then attends over all N tokens
+# with H/P heads (RoPE is applied in that layout too, where every token's
+# grid position is global) and modulates ceil(N/P) tokens at the full model
+# width.  The all-to-alls themselves need more than one GPU and are not
+# part of these shapes.
+SP_WORKLOADS = {
+    "mid_sp2": Workload("mid_sp2", 5, (21, 30, 52), 0, 20, 128, "bf16", (44, 42, 42),
+                        oracle_rows=256, sp=2),
+    "large_sp2": Workload("large_sp2", 6, (21, 45, 80), 0, 20, 128, "bf16", (44, 42, 42),
+                          oracle_rows=256, sp=2),
+    "large_sp8": Workload("large_sp8", 7, (21, 45, 80), 0, 5, 128, "bf16", (44, 42, 42),
+                          oracle_rows=256, sp=8),
+    "mixed_sp2": Workload("mixed_sp2", 8, (21, 48, 85), 226, 24, 64, "bf16", (16, 24, 24),
+                          oracle_rows=256, sp=2),
+    "mixed_sp4": Workload("mixed_sp4", 9, (21, 48, 85), 226, 12, 64, "bf16", (16, 24, 24),
+                          oracle_rows=256, sp=4),
+}
+
+
+def get(name: str) -> Workload:
+    """A workload by name: one of WORKLOADS or SP_WORKLOADS."""
+    if name in WORKLOADS:
+        return WORKLOADS[name]
+    if name in SP_WORKLOADS:
+        return SP_WORKLOADS[name]
+    raise KeyError(f"unknown workload {name!r}; known: {sorted(WORKLOADS) + sorted(SP_WORKLOADS)}")
+
 
 # The measured workload: 75,600 tokens, 40 heads x 128.
 BENCH_WORKLOAD = "large"

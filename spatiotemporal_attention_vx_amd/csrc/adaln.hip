@@ -23,31 +23,6 @@ template <bool BF16> struct AdaTraits;
 template <> struct AdaTraits<true> { static constexpr int EPC = 8; };   // bf16 per 16 B
 template <> struct AdaTraits<false> { static constexpr int EPC = 4; };  // f32 per 16 B
 
-template <bool BF16>
-__device__ __forceinline__ void unpack(const u32x4_t& v, float* f) {
-    if constexpr (BF16) {
-        const uint32_t w[4] = {v[0], v[1], v[2], v[3]};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) { f[2 * i] = bf16_lo(w[i]); f[2 * i + 1] = bf16_hi(w[i]); }
-    } else {
-        f[0] = __uint_as_float(v[0]); f[1] = __uint_as_float(v[1]);
-        f[2] = __uint_as_float(v[2]); f[3] = __uint_as_float(v[3]);
-    }
-}
-
-template <bool BF16>
-__device__ __forceinline__ u32x4_t pack(const float* f) {
-    u32x4_t r;
-    if constexpr (BF16) {
-        r[0] = pack_bf16x2(f[0], f[1]); r[1] = pack_bf16x2(f[2], f[3]);
-        r[2] = pack_bf16x2(f[4], f[5]); r[3] = pack_bf16x2(f[6], f[7]);
-    } else {
-        r[0] = __float_as_uint(f[0]); r[1] = __float_as_uint(f[1]);
-        r[2] = __float_as_uint(f[2]); r[3] = __float_as_uint(f[3]);
-    }
-    return r;
-}
-
 // Chan et al. merge of two (count, mean, M2) summaries.
 __device__ __forceinline__ void chan_merge(float& n, float& mean, float& m2,
                                            float nb, float meanb, float m2b) {
@@ -160,7 +135,7 @@ void adaln_kernel(const u32x4_t* x, const u32x4_t* __restrict__ shift,
     for (int j = 0; j < K; ++j) {
         if (valid(j)) {
             float f[EPC], mj, qj;
-            unpack<BF16>(xv[j], f);
+            unpack_chunk<BF16>(xv[j], f);
             chunk_stats<EPC>(f, mj, qj);
             if (j == 0) {
                 mean = mj;
@@ -196,15 +171,15 @@ void adaln_kernel(const u32x4_t* x, const u32x4_t* __restrict__ shift,
         const int c = lane + 64 * j;
         if (valid(j)) {
             float fx[EPC], fs[EPC], fc[EPC], out[EPC];
-            unpack<BF16>(xv[j], fx);
-            unpack<BF16>(sh[j], fs);
-            unpack<BF16>(sc[j], fc);
+            unpack_chunk<BF16>(xv[j], fx);
+            unpack_chunk<BF16>(sh[j], fs);
+            unpack_chunk<BF16>(sc[j], fc);
 #pragma unroll
             for (int e = 0; e < EPC; ++e) {
                 const float nrm = (fx[e] - mean) * rstd;
                 out[e] = __builtin_fmaf(nrm, 1.0f + fc[e], fs[e]);
             }
-            __builtin_nontemporal_store(pack<BF16>(out), y + base + c);
+            __builtin_nontemporal_store(pack_chunk<BF16>(out), y + base + c);
         }
     }
 }

@@ -70,9 +70,11 @@ struct FaArgs {
     const uint16_t* v;
     uint16_t* o;
     float* lse;
-    int64_t n;             // tokens
-    int64_t row_stride;    // elements between consecutive tokens (heads * D)
-    int64_t batch_stride;  // elements between batch entries (n * heads * D)
+    int64_t nq;               // query tokens
+    int64_t nk;               // key/value tokens
+    int64_t row_stride;       // elements between consecutive tokens (heads * D)
+    int64_t batch_stride;     // elements between batch entries of q and o (nq * heads * D)
+    int64_t kv_batch_stride;  // elements between batch entries of k and v (nk * heads * D)
     int heads;
     int n_qtiles;
     int64_t total_tiles;
@@ -174,9 +176,9 @@ __device__ __forceinline__ void load_q_fragment(const FaArgs& a, const uint16_t*
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
         uint4 w = {0u, 0u, 0u, 0u};
-        if (qi < a.n) w = *(const uint4*)(qb + qi * a.row_stride + ks * 16 + g * 8);
+        if (qi < a.nq) w = *(const uint4*)(qb + qi * a.row_stride + ks * 16 + g * 8);
         uint32_t u[4] = {w.x, w.y, w.z, w.w};
-        if (a.use_rope && qi < a.n) {
+        if (a.use_rope && qi < a.nq) {
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
                 const int pair = (ks * 16 + g * 8) / 2 + m;
@@ -217,10 +219,11 @@ void fa_fwd_bf16_kernel(FaArgs a) {
     const int h = (int)(bh % a.heads);
     const int64_t b = bh / a.heads;
     const int64_t off = b * a.batch_stride + (int64_t)h * D;
-    const uint16_t* kb = a.k + off;
-    const uint16_t* vb = a.v + off;
-    const int64_t n = a.n;
-    const int nt = (int)((n + FA_BC - 1) / FA_BC);
+    const int64_t kv_off = b * a.kv_batch_stride + (int64_t)h * D;
+    const uint16_t* kb = a.k + kv_off;
+    const uint16_t* vb = a.v + kv_off;
+    const int64_t nq = a.nq, nk = a.nk;
+    const int nt = (int)((nk + FA_BC - 1) / FA_BC);
 
     // query group qg of this wave: rows (wave * QG + qg) * 32 + l32 of the tile
     int64_t qi[QG];
@@ -250,13 +253,13 @@ void fa_fwd_bf16_kernel(FaArgs a) {
 
     auto load_k = [&](int t) {
         const int64_t kv0 = (int64_t)t * FA_BC;
-        const __amdgpu_buffer_rsrc_t r = buffer_rsrc(kb + kv0 * a.row_stride, (n - kv0) * row_bytes);
+        const __amdgpu_buffer_rsrc_t r = buffer_rsrc(kb + kv0 * a.row_stride, (nk - kv0) * row_bytes);
 #pragma unroll
         for (int i = 0; i < S::KCH; ++i) kreg[i] = __builtin_amdgcn_raw_buffer_load_b128(r, koff[i], 0, 0);
     };
     auto load_v = [&](int t) {
         const int64_t kv0 = (int64_t)t * FA_BC;
-        const __amdgpu_buffer_rsrc_t r = buffer_rsrc(vb + kv0 * a.row_stride, (n - kv0) * row_bytes);
+        const __amdgpu_buffer_rsrc_t r = buffer_rsrc(vb + kv0 * a.row_stride, (nk - kv0) * row_bytes);
 #pragma unroll
         for (int s = 0; s < S::KPT; ++s) {
             const auto w = __builtin_amdgcn_raw_buffer_load_b64(r, voff[s], 0, 0);
@@ -309,7 +312,7 @@ void fa_fwd_bf16_kernel(FaArgs a) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 const int64_t key = kv0 + kb2 * 32 + 8 * (i >> 2) + 4 * g + (i & 3);
-                if (key >= n) s[kb2][i] = -__builtin_inff();
+                if (key >= nk) s[kb2][i] = -__builtin_inff();
             }
     };
     auto row_max = [&](const f32x16_t* s) {
@@ -332,7 +335,7 @@ void fa_fwd_bf16_kernel(FaArgs a) {
         l_run[qg] = 0.f;
         mx_next[qg] = 0.f;
     }
-    const bool tail = (n % FA_BC) != 0;
+    const bool tail = (nk % FA_BC) != 0;
 
     // ---- prologue: K(0), K(1), K(2) and V(0) into LDS; S(0); m from tile 0
     f32x16_t sA[QG][2], sB[QG][2];
@@ -523,7 +526,7 @@ void fa_fwd_bf16_kernel(FaArgs a) {
     for (int qg = 0; qg < QG; ++qg) {
         const float l_tot = half_sum(l_run[qg]);
         const float inv = 1.0f / l_tot;
-        if (qi[qg] < n) {
+        if (qi[qg] < nq) {
             uint16_t* ob = a.o + off + qi[qg] * a.row_stride;
 #pragma unroll
             for (int db = 0; db < NDB; ++db)
@@ -536,7 +539,7 @@ void fa_fwd_bf16_kernel(FaArgs a) {
                     *(uint2*)(ob + db * 32 + 8 * r + 4 * g) = w;
                 }
             if (a.lse != nullptr && g == 0)
-                a.lse[bh * n + qi[qg]] = (m_ref[qg] + __builtin_log2f(l_tot)) * 0.69314718055994531f;
+                a.lse[bh * nq + qi[qg]] = (m_ref[qg] + __builtin_log2f(l_tot)) * 0.69314718055994531f;
         }
     }
 }
@@ -590,10 +593,11 @@ void fa_fwd_bf16_dma_kernel(FaArgs a) {
     const int h = (int)(bh % a.heads);
     const int64_t b = bh / a.heads;
     const int64_t off = b * a.batch_stride + (int64_t)h * D;
-    const uint16_t* kb = a.k + off;
-    const uint16_t* vb = a.v + off;
-    const int64_t n = a.n;
-    const int nt = (int)((n + FA_BC - 1) / FA_BC);
+    const int64_t kv_off = b * a.kv_batch_stride + (int64_t)h * D;
+    const uint16_t* kb = a.k + kv_off;
+    const uint16_t* vb = a.v + kv_off;
+    const int64_t nq = a.nq, nk = a.nk;
+    const int nt = (int)((nk + FA_BC - 1) / FA_BC);
 
     const int64_t qi = (int64_t)qt * BR + wave * 32 + l32;
     bf16x8_t qf[NKK];
@@ -618,7 +622,7 @@ void fa_fwd_bf16_dma_kernel(FaArgs a) {
     // and no buffer is a DMA target while any wave may still read it.
     auto dma_one = [&](const uint16_t* base, int t, lds_u8* buf, int m) {
         const int64_t kv0 = (int64_t)t * FA_BC;
-        const __amdgpu_buffer_rsrc_t r = buffer_rsrc(base + kv0 * a.row_stride, (n - kv0) * row_bytes);
+        const __amdgpu_buffer_rsrc_t r = buffer_rsrc(base + kv0 * a.row_stride, (nk - kv0) * row_bytes);
         const uint32_t dst = (uint32_t)(uintptr_t)(buf + (swave * NI + m) * 1024);
         __asm__ volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                          :
@@ -669,8 +673,8 @@ void fa_fwd_bf16_dma_kernel(FaArgs a) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             const int64_t key = kv0 + 8 * (i >> 2) + 4 * g + (i & 3);
-            if (key >= n) s0[i] = -__builtin_inff();
-            if (key + 32 >= n) s1[i] = -__builtin_inff();
+            if (key >= nk) s0[i] = -__builtin_inff();
+            if (key + 32 >= nk) s1[i] = -__builtin_inff();
         }
     };
     auto row_max = [&](const f32x16_t& s0, const f32x16_t& s1) {
@@ -685,7 +689,7 @@ void fa_fwd_bf16_dma_kernel(FaArgs a) {
     for (int i = 0; i < NDB; ++i) acc[i] = f32x16_t{};
     f32x16_t negm = f32x16_t{};   // -m in every slot: the C operand of the first k-step
     float m_ref, l_run = 0.f, mx_next = 0.f;
-    const bool tail = (n % FA_BC) != 0;
+    const bool tail = (nk % FA_BC) != 0;
 
     // ---- prologue: K(0..2), V(0..1) into LDS; S(0); m from tile 0
     // S tiles rotate through three register blocks: step t reads S(t) from
@@ -828,7 +832,7 @@ void fa_fwd_bf16_dma_kernel(FaArgs a) {
 
     const float l_tot = half_sum(l_run);
     const float inv = 1.0f / l_tot;
-    if (qi < n) {
+    if (qi < nq) {
         uint16_t* ob = a.o + off + qi * a.row_stride;
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
@@ -841,7 +845,7 @@ void fa_fwd_bf16_dma_kernel(FaArgs a) {
                 *(uint2*)(ob + db * 32 + 8 * r + 4 * g) = w;
             }
         if (a.lse != nullptr && g == 0)
-            a.lse[bh * n + qi] = (m_ref + __builtin_log2f(l_tot)) * 0.69314718055994531f;
+            a.lse[bh * nq + qi] = (m_ref + __builtin_log2f(l_tot)) * 0.69314718055994531f;
     }
 }
 
@@ -868,20 +872,21 @@ void fa_fwd_f32_kernel(FaArgs a) {
     const int h = (int)(bh % a.heads);
     const int64_t b = bh / a.heads;
     const int64_t off = b * a.batch_stride + (int64_t)h * D;
+    const int64_t kv_off = b * a.kv_batch_stride + (int64_t)h * D;
     const float* qb = (const float*)a.q + off;
-    const float* kbp = (const float*)a.k + off;
-    const float* vbp = (const float*)a.v + off;
-    const int64_t n = a.n;
+    const float* kbp = (const float*)a.k + kv_off;
+    const float* vbp = (const float*)a.v + kv_off;
+    const int64_t nq = a.nq, nk = a.nk;
 
     const int part = tid % TPQ;
     const int64_t qi = (int64_t)qt * QPB + tid / TPQ;
     float qv[32], acc[32];
 #pragma unroll
     for (int e = 0; e < 32; ++e) {
-        qv[e] = qi < n ? qb[qi * a.row_stride + part * 32 + e] : 0.f;
+        qv[e] = qi < nq ? qb[qi * a.row_stride + part * 32 + e] : 0.f;
         acc[e] = 0.f;
     }
-    if (a.use_rope && qi < n) {
+    if (a.use_rope && qi < nq) {
 #pragma unroll
         for (int m = 0; m < 16; ++m) {
             int pos, j, width;
@@ -894,13 +899,13 @@ void fa_fwd_f32_kernel(FaArgs a) {
     }
 
     float m_run = -__builtin_inff(), l_run = 0.f;
-    for (int64_t kv0 = 0; kv0 < n; kv0 += FA32_BC) {
+    for (int64_t kv0 = 0; kv0 < nk; kv0 += FA32_BC) {
         __syncthreads();
         for (int i = tid; i < FA32_BC * D / 4; i += 256) {
             const int key = i / (D / 4), col = i % (D / 4);
             const int64_t kk = kv0 + key;
             float4 kv = {0.f, 0.f, 0.f, 0.f}, vv = {0.f, 0.f, 0.f, 0.f};
-            if (kk < n) {
+            if (kk < nk) {
                 kv = *(const float4*)(kbp + kk * a.row_stride + col * 4);
                 vv = *(const float4*)(vbp + kk * a.row_stride + col * 4);
             }
@@ -908,7 +913,7 @@ void fa_fwd_f32_kernel(FaArgs a) {
             *(float4*)(vs + key * D + col * 4) = vv;
         }
         __syncthreads();
-        const int cnt = (int)((n - kv0) < FA32_BC ? (n - kv0) : FA32_BC);
+        const int cnt = (int)((nk - kv0) < FA32_BC ? (nk - kv0) : FA32_BC);
         for (int j = 0; j < cnt; ++j) {
             const float* kr = ks + j * D + part * 32;
             float s = 0.f;
@@ -927,12 +932,12 @@ void fa_fwd_f32_kernel(FaArgs a) {
             m_run = m_new;
         }
     }
-    if (qi < n) {
+    if (qi < nq) {
         float* ob = (float*)a.o + off + qi * a.row_stride + part * 32;
         const float inv = 1.0f / l_run;
 #pragma unroll
         for (int e = 0; e < 32; ++e) ob[e] = acc[e] * inv;
-        if (a.lse != nullptr && part == 0) a.lse[bh * n + qi] = m_run + logf(l_run);
+        if (a.lse != nullptr && part == 0) a.lse[bh * nq + qi] = m_run + logf(l_run);
     }
 }
 
@@ -946,17 +951,20 @@ int flash_attn_rows_per_workgroup(bool bf16, int64_t head_dim) {
 }
 
 hipError_t launch_flash_attn(const void* q, const void* k, const void* v, void* o, float* lse,
-                             int64_t batch, int64_t n, int64_t heads, int64_t head_dim,
-                             float scale, const RopeArgs* rope, bool bf16, hipStream_t st) {
+                             int64_t batch, int64_t nq, int64_t nk, int64_t heads,
+                             int64_t head_dim, float scale, const RopeArgs* rope, bool bf16,
+                             hipStream_t st) {
     FaArgs a;
     a.q = (const uint16_t*)q;
     a.k = (const uint16_t*)k;
     a.v = (const uint16_t*)v;
     a.o = (uint16_t*)o;
     a.lse = lse;
-    a.n = n;
+    a.nq = nq;
+    a.nk = nk;
     a.row_stride = heads * head_dim;
-    a.batch_stride = n * heads * head_dim;
+    a.batch_stride = nq * heads * head_dim;
+    a.kv_batch_stride = nk * heads * head_dim;
     a.heads = (int)heads;
     a.scale = scale;
     a.scale_log2 = scale * 1.4426950408889634f;
@@ -965,7 +973,7 @@ hipError_t launch_flash_attn(const void* q, const void* k, const void* v, void* 
     else a.rope = RopeArgs{1, 1, 1, 0, 0, 0, 0, 1.f};
 
     const int rows_per_wg = flash_attn_rows_per_workgroup(bf16, head_dim);
-    a.n_qtiles = (int)((n + rows_per_wg - 1) / rows_per_wg);
+    a.n_qtiles = (int)((nq + rows_per_wg - 1) / rows_per_wg);
     a.total_tiles = batch * heads * a.n_qtiles;
     const dim3 grid((unsigned)a.total_tiles);
     if (bf16) {

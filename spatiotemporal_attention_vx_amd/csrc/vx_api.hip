@@ -18,8 +18,12 @@ hipError_t launch_adaln(const void* x, const void* shift, const void* scale, voi
 hipError_t launch_rope3d(void* q, void* k, int64_t batch, int64_t n_tokens, int64_t heads,
                          int64_t head_dim, const RopeArgs& r, bool bf16, hipStream_t st);
 hipError_t launch_flash_attn(const void* q, const void* k, const void* v, void* o, float* lse,
-                             int64_t batch, int64_t n, int64_t heads, int64_t head_dim,
-                             float scale, const RopeArgs* rope, bool bf16, hipStream_t st);
+                             int64_t batch, int64_t nq, int64_t nk, int64_t heads,
+                             int64_t head_dim, float scale, const RopeArgs* rope, bool bf16,
+                             hipStream_t st);
+hipError_t launch_attn_merge(const void* oa, const float* lsea, const void* ob, const float* lseb,
+                             void* o, float* lse, int64_t batch, int64_t n, int64_t heads,
+                             int64_t head_dim, bool bf16, hipStream_t st);
 int flash_attn_rows_per_workgroup(bool bf16, int64_t head_dim);
 }  // namespace vx
 
@@ -97,6 +101,45 @@ int launched(hipError_t e, const char* what) {
     return ok();
 }
 
+// Checks shared by the two attention entry points; nq == nk for the
+// self-attention one.
+int flash_attn(const char* fn, const void* q, const void* k, const void* v, void* o, float* lse,
+               int64_t batch, int64_t nq, int64_t nk, int64_t heads, int64_t head_dim,
+               float softmax_scale, const vx_rope3d_desc* rope_q, int dt, void* hip_stream) {
+    if (!q || !k || !v || !o) return fail(VX_ERR_NULL, "%s: NULL tensor", fn);
+    if (int e = check_dtype(fn, dt)) return e;
+    if (batch <= 0 || nq <= 0 || nk <= 0 || heads <= 0 || head_dim <= 0)
+        return fail(VX_ERR_INVALID, "%s: sizes must be positive", fn);
+    if (!std::isfinite(softmax_scale))
+        return fail(VX_ERR_INVALID, "%s: softmax_scale must be finite", fn);
+    if (head_dim != 64 && head_dim != 128)
+        return fail(VX_ERR_UNSUPPORTED, "%s: head_dim %lld (64 or 128 only)", fn, (long long)head_dim);
+    vx::RopeArgs r;
+    if (rope_q)
+        if (int e = check_rope(fn, rope_q, nq, head_dim, &r)) return e;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
+        (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)))
+        return fail(VX_ERR_ALIGN, "%s: q, k, v, o must be 16-byte aligned, lse 4-byte", fn);
+    const bool bf16 = dt == VX_BF16;
+    const int64_t esz = bf16 ? 2 : 4;
+    int64_t qbytes, kbytes, lse_bytes, rows;
+    const int64_t per_wg = vx::flash_attn_rows_per_workgroup(bf16, head_dim);
+    if (!mul_ok(qbytes, {batch, nq, heads, head_dim, esz}) ||
+        !mul_ok(kbytes, {batch, nk, heads, head_dim, esz}) ||
+        !mul_ok(lse_bytes, {batch, heads, nq, 4}) ||
+        !mul_ok(rows, {batch, heads, (nq + per_wg - 1) / per_wg}) || rows > INT32_MAX)
+        return fail(VX_ERR_INVALID, "%s: size overflow", fn);
+    if (overlaps(o, qbytes, q, qbytes) || overlaps(o, qbytes, k, kbytes) || overlaps(o, qbytes, v, kbytes))
+        return fail(VX_ERR_INVALID, "%s: o overlaps q, k or v", fn);
+    if (lse && (overlaps(lse, lse_bytes, q, qbytes) || overlaps(lse, lse_bytes, k, kbytes) ||
+                overlaps(lse, lse_bytes, v, kbytes) || overlaps(lse, lse_bytes, o, qbytes)))
+        return fail(VX_ERR_INVALID, "%s: lse overlaps a tensor", fn);
+    const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)head_dim);
+    return launched(vx::launch_flash_attn(q, k, v, o, lse, batch, nq, nk, heads, head_dim, scale,
+                                          rope_q ? &r : nullptr, bf16, (hipStream_t)hip_stream),
+                    fn);
+}
+
 }  // namespace
 
 extern "C" {
@@ -161,42 +204,57 @@ int vx_flash_attn_fwd(const void* q, const void* k, const void* v, void* o, floa
                       int64_t batch, int64_t n_tokens, int64_t heads, int64_t head_dim,
                       float softmax_scale, const vx_rope3d_desc* rope_q, int dt,
                       void* hip_stream) {
-    if (!q || !k || !v || !o) return fail(VX_ERR_NULL, "vx_flash_attn_fwd: NULL tensor");
-    if (int e = check_dtype("vx_flash_attn_fwd", dt)) return e;
+    return flash_attn("vx_flash_attn_fwd", q, k, v, o, lse, batch, n_tokens, n_tokens, heads,
+                      head_dim, softmax_scale, rope_q, dt, hip_stream);
+}
+
+int vx_flash_attn_fwd_kv(const void* q, const void* k, const void* v, void* o, float* lse,
+                         int64_t batch, int64_t n_q, int64_t n_kv, int64_t heads,
+                         int64_t head_dim, float softmax_scale, const vx_rope3d_desc* rope_q,
+                         int dt, void* hip_stream) {
+    return flash_attn("vx_flash_attn_fwd_kv", q, k, v, o, lse, batch, n_q, n_kv, heads, head_dim,
+                      softmax_scale, rope_q, dt, hip_stream);
+}
+
+int vx_attn_merge2(const void* o_a, const float* lse_a, const void* o_b, const float* lse_b,
+                   void* o, float* lse, int64_t batch, int64_t n_tokens, int64_t heads,
+                   int64_t head_dim, int dt, void* hip_stream) {
+    const char* fn = "vx_attn_merge2";
+    if (!o_a || !lse_a || !o_b || !lse_b || !o) return fail(VX_ERR_NULL, "%s: NULL tensor", fn);
+    if (int e = check_dtype(fn, dt)) return e;
     if (batch <= 0 || n_tokens <= 0 || heads <= 0 || head_dim <= 0)
-        return fail(VX_ERR_INVALID, "vx_flash_attn_fwd: sizes must be positive");
-    if (!std::isfinite(softmax_scale))
-        return fail(VX_ERR_INVALID, "vx_flash_attn_fwd: softmax_scale must be finite");
+        return fail(VX_ERR_INVALID, "%s: sizes must be positive", fn);
     if (head_dim != 64 && head_dim != 128)
-        return fail(VX_ERR_UNSUPPORTED, "vx_flash_attn_fwd: head_dim %lld (64 or 128 only)",
-                    (long long)head_dim);
-    vx::RopeArgs r;
-    if (rope_q)
-        if (int e = check_rope("vx_flash_attn_fwd", rope_q, n_tokens, head_dim, &r)) return e;
-    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
-        (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)))
-        return fail(VX_ERR_ALIGN, "vx_flash_attn_fwd: q, k, v, o must be 16-byte aligned, lse 4-byte");
+        return fail(VX_ERR_UNSUPPORTED, "%s: head_dim %lld (64 or 128 only)", fn, (long long)head_dim);
+    const uintptr_t lmask = 3u;
+    if (!aligned16(o_a) || !aligned16(o_b) || !aligned16(o) ||
+        (reinterpret_cast<uintptr_t>(lse_a) & lmask) || (reinterpret_cast<uintptr_t>(lse_b) & lmask) ||
+        (lse && (reinterpret_cast<uintptr_t>(lse) & lmask)))
+        return fail(VX_ERR_ALIGN, "%s: o tensors must be 16-byte aligned, lse 4-byte", fn);
     const bool bf16 = dt == VX_BF16;
-    const int64_t esz = bf16 ? 2 : 4;
-    int64_t bytes, lse_bytes, rows;
-    const int64_t per_wg = vx::flash_attn_rows_per_workgroup(bf16, head_dim);
-    if (!mul_ok(bytes, {batch, n_tokens, heads, head_dim, esz}) ||
-        !mul_ok(lse_bytes, {batch, heads, n_tokens, 4}) ||
-        !mul_ok(rows, {batch, heads, (n_tokens + per_wg - 1) / per_wg}) || rows > INT32_MAX)
-        return fail(VX_ERR_INVALID, "vx_flash_attn_fwd: size overflow");
-    if (overlaps(o, bytes, q, bytes) || overlaps(o, bytes, k, bytes) || overlaps(o, bytes, v, bytes))
-        return fail(VX_ERR_INVALID, "vx_flash_attn_fwd: o overlaps q, k or v");
-    if (lse && (overlaps(lse, lse_bytes, q, bytes) || overlaps(lse, lse_bytes, k, bytes) ||
-                overlaps(lse, lse_bytes, v, bytes) || overlaps(lse, lse_bytes, o, bytes)))
-        return fail(VX_ERR_INVALID, "vx_flash_attn_fwd: lse overlaps a tensor");
-    const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)head_dim);
-    return launched(vx::launch_flash_attn(q, k, v, o, lse, batch, n_tokens, heads, head_dim, scale,
-                                          rope_q ? &r : nullptr, bf16, (hipStream_t)hip_stream),
-                    "vx_flash_attn_fwd");
+    int64_t bytes, lse_bytes, chunks;
+    if (!mul_ok(bytes, {batch, n_tokens, heads, head_dim, bf16 ? 2 : 4}) ||
+        !mul_ok(lse_bytes, {batch, heads, n_tokens, 4}) || !mul_ok(chunks, {bytes / 16}) ||
+        (chunks + 255) / 256 > INT32_MAX)
+        return fail(VX_ERR_INVALID, "%s: size overflow", fn);
+    // o may be o_a or o_b exactly (in place); any other overlap is invalid.
+    // The same holds for lse against lse_a / lse_b.
+    if ((o != o_a && overlaps(o, bytes, o_a, bytes)) || (o != o_b && overlaps(o, bytes, o_b, bytes)))
+        return fail(VX_ERR_INVALID, "%s: o overlaps o_a or o_b other than exactly", fn);
+    if (lse && ((lse != lse_a && overlaps(lse, lse_bytes, lse_a, lse_bytes)) ||
+                (lse != lse_b && overlaps(lse, lse_bytes, lse_b, lse_bytes))))
+        return fail(VX_ERR_INVALID, "%s: lse overlaps lse_a or lse_b other than exactly", fn);
+    if (overlaps(o, bytes, lse_a, lse_bytes) || overlaps(o, bytes, lse_b, lse_bytes) ||
+        (lse && (overlaps(lse, lse_bytes, o_a, bytes) || overlaps(lse, lse_bytes, o_b, bytes) ||
+                 overlaps(lse, lse_bytes, o, bytes))))
+        return fail(VX_ERR_INVALID, "%s: an output overlaps a tensor of the other kind", fn);
+    return launched(vx::launch_attn_merge(o_a, lse_a, o_b, lse_b, o, lse, batch, n_tokens, heads,
+                                          head_dim, bf16, (hipStream_t)hip_stream),
+                    fn);
 }
 
 const char* vx_last_error(void) { return g_error.c_str(); }
 
-int vx_version(void) { return 100; }
+int vx_version(void) { return 200; }
 
 }  // extern "C"

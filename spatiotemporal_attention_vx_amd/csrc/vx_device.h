@@ -25,6 +25,32 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
     return __builtin_bit_cast(uint32_t, h);
 }
 
+// A 16-byte chunk as floats: 8 bf16 (exact widening) or 4 f32.
+template <bool BF16>
+__device__ __forceinline__ void unpack_chunk(const u32x4_t& v, float* f) {
+    if constexpr (BF16) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { f[2 * i] = bf16_lo(v[i]); f[2 * i + 1] = bf16_hi(v[i]); }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) f[i] = __uint_as_float(v[i]);
+    }
+}
+
+// Floats back to one 16-byte chunk (bf16: round to nearest even).
+template <bool BF16>
+__device__ __forceinline__ u32x4_t pack_chunk(const float* f) {
+    u32x4_t r;
+    if constexpr (BF16) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) r[i] = pack_bf16x2(f[2 * i], f[2 * i + 1]);
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) r[i] = __float_as_uint(f[i]);
+    }
+    return r;
+}
+
 // RoPE geometry of one call, in kernel-argument form.
 struct RopeArgs {
     int32_t T, H, W;

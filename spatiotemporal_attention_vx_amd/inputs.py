@@ -128,9 +128,15 @@ def attention_inputs(wl, seed: int = 0):
 
 
 def adaln_inputs(wl, seed: int = 0):
-    """x ~ N(0,1), shift ~ N(0,0.1), scale ~ N(0,0.1); each [batch*N, hidden]."""
-    return (tensor(wl, seed, T_X, 1.0), tensor(wl, seed, T_SHIFT, 0.1),
-            tensor(wl, seed, T_SCALE, 0.1))
+    """x ~ N(0,1), shift ~ N(0,0.1), scale ~ N(0,0.1); each [batch*rows, width].
+
+    rows and width are the tokens and model width one GPU modulates
+    (``wl.adaln_rows``, ``wl.adaln_hidden``): N and heads*head_dim unless
+    ``wl`` is one GPU's share of a sequence-parallel run.
+    """
+    n = wl.adaln_rows * wl.batch
+    return tuple(normal_rows(seed, wl.config_id, t, n, wl.adaln_hidden, std, None, wl.dtype)
+                 for t, std in ((T_X, 1.0), (T_SHIFT, 0.1), (T_SCALE, 0.1)))
 
 
 def sample_rows(wl, seed: int = 0, count: int = 0) -> np.ndarray:

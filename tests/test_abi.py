@@ -135,6 +135,43 @@ def test_attention_rejects(ptrs, n, d, scale, rope, dt, code):
     assert lib.vx_last_error().decode().startswith("vx_flash_attn_fwd")
 
 
+@host_only
+@pytest.mark.parametrize("ptrs,nq,nk,d,rope,code", [
+    ((None, A + MB, A + 2 * MB, A + 3 * MB, None), 24, 30, 64, None, NULL),
+    ((A, A + MB, A + 2 * MB, A + 3 * MB, None), 24, 0, 64, None, INVALID),
+    ((A, A + MB, A + 2 * MB, A + 3 * MB, None), 0, 30, 64, None, INVALID),
+    ((A, A + MB, A + 2 * MB, A + 3 * MB, None), 24, 30, 96, None, UNSUPPORTED),
+    ((A, A + MB, A + 2 * MB, A + 3 * MB, None), 24, 30, 64, _rope(T=3), INVALID),  # grid != n_q
+    ((A, A + MB, A + 2 * MB, A + MB + 64, None), 24, 30, 64, None, INVALID),     # o overlaps k
+    ((A, A + MB, A + 2 * MB, A + 3 * MB + 8, None), 24, 30, 64, None, ALIGN),
+])
+def test_attention_kv_rejects(ptrs, nq, nk, d, rope, code):
+    lib = binding.load()
+    r = ctypes.byref(rope) if rope is not None else None
+    assert lib.vx_flash_attn_fwd_kv(*ptrs, 1, nq, nk, 2, d, 0.0, r, 1, None) == code
+    assert lib.vx_last_error().decode().startswith("vx_flash_attn_fwd_kv")
+
+
+@host_only
+@pytest.mark.parametrize("ptrs,n,d,dt,code", [
+    ((None, A + MB, A + 2 * MB, A + 3 * MB, A + 4 * MB, A + 5 * MB), 24, 64, 1, NULL),
+    ((A, None, A + 2 * MB, A + 3 * MB, A + 4 * MB, A + 5 * MB), 24, 64, 1, NULL),
+    ((A, A + MB, A + 2 * MB, A + 3 * MB, None, A + 5 * MB), 24, 64, 1, NULL),
+    ((A, A + MB, A + 2 * MB, A + 3 * MB, A + 4 * MB, A + 5 * MB), 0, 64, 1, INVALID),
+    ((A, A + MB, A + 2 * MB, A + 3 * MB, A + 4 * MB, A + 5 * MB), 24, 64, 3, INVALID),
+    ((A, A + MB, A + 2 * MB, A + 3 * MB, A + 4 * MB, A + 5 * MB), 24, 32, 1, UNSUPPORTED),
+    ((A + 4, A + MB, A + 2 * MB, A + 3 * MB, A + 4 * MB, A + 5 * MB), 24, 64, 1, ALIGN),
+    ((A, A + MB + 2, A + 2 * MB, A + 3 * MB, A + 4 * MB, A + 5 * MB), 24, 64, 1, ALIGN),
+    ((A, A + MB, A + 2 * MB, A + 3 * MB, A + 64, A + 5 * MB), 24, 64, 1, INVALID),   # o inside o_a
+    ((A, A + MB, A + 2 * MB, A + 3 * MB, A + 4 * MB, A + MB + 4), 24, 64, 1, INVALID),  # lse inside lse_a
+    ((A, A + MB, A + 2 * MB, A + 3 * MB, A + MB, A + 5 * MB), 24, 64, 1, INVALID),   # o on lse_a
+])
+def test_attn_merge_rejects(ptrs, n, d, dt, code):
+    lib = binding.load()
+    assert lib.vx_attn_merge2(*ptrs, 1, n, 2, d, dt, None) == code
+    assert lib.vx_last_error().decode().startswith("vx_attn_merge2")
+
+
 def test_binding_refuses_mismatched_tensors():
     import torch
     x = torch.zeros(4, 64)

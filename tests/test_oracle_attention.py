@@ -125,3 +125,62 @@ def test_rope_with_prefix_rows():
     o2, l2 = oracle.attention(qr, kr, v, rows=rows)
     np.testing.assert_allclose(o, o2, atol=1e-13)
     np.testing.assert_allclose(l, l2, atol=1e-13)
+
+
+# ---- queries and keys from different token sets; merging key-split parts
+
+def test_cross_attention_matches_library_sdpa():
+    g = np.random.default_rng(11)
+    q = g.standard_normal((23, 2, 64))
+    k, v = g.standard_normal((70, 2, 64)), g.standard_normal((70, 2, 64))
+    o, lse = oracle.attention(q, k, v)
+    t = lambda a: torch.from_numpy(a).permute(1, 0, 2)[None]
+    ref = torch.nn.functional.scaled_dot_product_attention(t(q), t(k), t(v))
+    np.testing.assert_allclose(o, ref[0].permute(1, 0, 2).numpy(), rtol=0, atol=1e-12)
+    s = np.einsum("qhd,khd->hqk", q, k) / 8.0
+    np.testing.assert_allclose(lse, scipy.special.logsumexp(s, axis=-1), rtol=0, atol=1e-12)
+
+
+def test_cross_attention_single_key_returns_its_value():
+    g = np.random.default_rng(12)
+    q = g.standard_normal((9, 3, 64))
+    k, v = g.standard_normal((1, 3, 64)), g.standard_normal((1, 3, 64))
+    o, lse = oracle.attention(q, k, v)
+    np.testing.assert_array_equal(o, np.broadcast_to(v, o.shape))
+    np.testing.assert_allclose(lse, np.einsum("qhd,hd->hq", q, k[0]) / 8.0, rtol=0, atol=1e-13)
+
+
+@pytest.mark.parametrize("split", [1, 17, 39])
+def test_merge_of_key_split_equals_full_attention(split):
+    q, k, v = _qkv(40, 3, 64, seed=13)
+    o_a, l_a = oracle.attention(q, k[:split], v[:split])
+    o_b, l_b = oracle.attention(q, k[split:], v[split:])
+    o, lse = oracle.merge_lse(o_a, l_a, o_b, l_b)
+    ref, rl = oracle.attention(q, k, v)
+    np.testing.assert_allclose(o, ref, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, rl, rtol=0, atol=1e-12)
+
+
+def test_merge_is_associative_and_symmetric():
+    q, k, v = _qkv(45, 2, 64, seed=14)
+    parts = [oracle.attention(q, k[a:b], v[a:b]) for a, b in ((0, 10), (10, 31), (31, 45))]
+    left = oracle.merge_lse(*oracle.merge_lse(*parts[0], *parts[1]), *parts[2])
+    right = oracle.merge_lse(*parts[0], *oracle.merge_lse(*parts[1], *parts[2]))
+    swapped = oracle.merge_lse(*parts[2], *oracle.merge_lse(*parts[1], *parts[0]))
+    for x in (right, swapped):
+        np.testing.assert_allclose(x[0], left[0], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(x[1], left[1], rtol=0, atol=1e-12)
+
+
+def test_merge_with_empty_part_and_with_itself():
+    q, k, v = _qkv(20, 2, 64, seed=15)
+    o, lse = oracle.attention(q, k, v)
+    empty_o, empty_l = np.zeros_like(o), np.full_like(lse, -np.inf)
+    mo, ml = oracle.merge_lse(o, lse, empty_o, empty_l)
+    np.testing.assert_array_equal(mo, o)
+    np.testing.assert_array_equal(ml, lse)
+    mo, ml = oracle.merge_lse(empty_o, empty_l, empty_o, empty_l)
+    assert np.all(mo == 0) and np.all(np.isneginf(ml))
+    mo, ml = oracle.merge_lse(o, lse, o, lse)      # the same keys twice: Z doubles
+    np.testing.assert_allclose(mo, o, rtol=0, atol=1e-14)
+    np.testing.assert_allclose(ml, lse + np.log(2.0), rtol=0, atol=1e-13)
