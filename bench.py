@@ -35,6 +35,15 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 METRIC = "flash-attn TFLOP/s + % bf16 MFMA peak at 75,600 tokens, 40 heads × d128"
 
 
+# AdaLN variants: (x dtype, table dtype, per-sample tables); y is bf16.
+ADALN_MODES = {
+    "token": ("bf16", "bf16", False),          # Wan2.2: a table row per token
+    "sample": ("bf16", "bf16", True),          # Wan2.1: a table row per sample
+    "f32-residual": ("f32", "bf16", False),    # residual stream kept in fp32
+    "f32-tables": ("bf16", "f32", False),      # modulation tables kept in fp32
+}
+
+
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
@@ -43,6 +52,8 @@ def parse():
     p.add_argument("--workload", default="large")
     p.add_argument("--rope", choices=["fused", "separate"], default="fused",
                    help="fused: K rotated by vx_rope3d_apply, Q inside the attention load")
+    p.add_argument("--adaln", choices=list(ADALN_MODES), default="token",
+                   help="AdaLN variant in the step: table layout and storage types")
     p.add_argument("--cpu-rows", type=int, default=512,
                    help="query rows of the oracle CPU baseline (0 = skip it)")
     p.add_argument("--copy-calibration", action="store_true",
@@ -119,14 +130,24 @@ def main():
     # ---- inputs: host generation (seeded), one copy to HBM
     t0 = time.perf_counter()
     q, k, v = inputs.attention_inputs(wl)
-    x, sh, sc = inputs.adaln_inputs(wl)
+    x, sh, sc = inputs.adaln_inputs(wl) if args.adaln == "token" else (None, None, None)
 
     def up(a):
         return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
 
+    def up_any(a):
+        return up(a) if a.dtype == np.uint16 else torch.from_numpy(a).to(dev)
+
     tq, tk, tv = up(q), up(k), up(v)
-    tx, tsh, tsc = up(x), up(sh), up(sc)
-    ty = torch.empty_like(tx)
+    x_dt, m_dt, per_sample = ADALN_MODES[args.adaln]
+    if args.adaln == "token":
+        tx, tsh, tsc = up(x), up(sh), up(sc)
+        ty = torch.empty_like(tx)
+    else:
+        x, sh, sc = inputs.adaln_inputs_ex(wl, x_dt, m_dt, per_sample)
+        tx, tsh, tsc = up_any(x), up_any(sh), up_any(sc)
+        ty = torch.empty(tx.shape, dtype=torch.bfloat16, device=dev)
+    adaln_bytes = sum(t.numel() * t.element_size() for t in (tx, tsh, tsc, ty))
     to = torch.empty_like(tq)
     gen_s = time.perf_counter() - t0
     desc = binding.RopeDesc.of(wl.grid, wl.split, wl.theta, wl.n_prefix)
@@ -139,7 +160,10 @@ def main():
         marks = [torch.cuda.Event(enable_timing=True) for _ in range(4)] if record else None
         if record:
             marks[0].record(stream)
-        binding.adaln_modulate(tx, tsh, tsc, ty, wl.eps, stream=stream)
+        if args.adaln == "token":
+            binding.adaln_modulate(tx, tsh, tsc, ty, wl.eps, stream=stream)
+        else:
+            binding.adaln_modulate_ex(tx, tsh, tsc, ty, wl.eps, stream=stream)
         if record:
             marks[1].record(stream)
         binding.rope3d_apply(None if fused else tq, tk, desc, stream=stream)
@@ -181,8 +205,10 @@ def main():
         "attn_tflops": round(attn_tflops, 2),
         "attn_exps": float(wl.n_tokens) ** 2 * wl.heads,
         "adaln_ms": round(ms["adaln"], 4),
-        "adaln_gbs": round(wl.adaln_bytes() / (ms["adaln"] * 1e-3) / 1e9, 1),
-        "adaln_hbm_frac": round(wl.adaln_bytes() / (ms["adaln"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+        "adaln_mode": args.adaln,
+        "adaln_bytes": adaln_bytes,
+        "adaln_gbs": round(adaln_bytes / (ms["adaln"] * 1e-3) / 1e9, 1),
+        "adaln_hbm_frac": round(adaln_bytes / (ms["adaln"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
         "rope_ms": round(ms["rope"], 4),
         "rope_tensors": "K" if fused else "Q,K",
         "rope_gbs": round(rope_bytes / (ms["rope"] * 1e-3) / 1e9, 1),

@@ -4,6 +4,7 @@
  * Three operations, one per step of a video diffusion-transformer block as
  * the vidax pages describe it:
  *   vx_adaln_modulate   per-token AdaLN modulation
+ *                       (vx_adaln_modulate_ex: per-sample tables, mixed dtypes)
  *   vx_rope3d_apply     3D rotary position embedding on Q and K
  *   vx_flash_attn_fwd   full non-causal attention, flash style
  * and, for attention whose keys are split into parts (sharded or in
@@ -92,6 +93,35 @@ typedef struct {
  */
 int vx_adaln_modulate(const void* x, const void* shift, const void* scale, void* y,
                       int64_t n_rows, int64_t hidden, float eps, int dt, void* hip_stream);
+
+/*
+ * AdaLN modulation with per-sample or per-token tables and mixed dtypes
+ * (vidax paper §3.1 and Table 1: Wan2.1 modulates all tokens of a sample
+ * with one scale and shift, Wan2.2 every token with its own; §3.2 "Weight
+ * import, precision, and verification": Wan2.1's residual stream and
+ * LTX-2.5's AdaLN tables stay in fp32, since bf16 there degrades the
+ * video).
+ *
+ *   y[b, n, :] = LN(x[b, n, :]) * (1 + scale[b, m, :]) + shift[b, m, :]
+ *
+ * with m = n when mod_tokens == n_tokens (per token) and m = 0 when
+ * mod_tokens == 1 (per sample, the row broadcast over the sample's tokens).
+ * LN as for vx_adaln_modulate.  x: [batch, n_tokens, hidden] of x_dt;
+ * shift, scale: [batch, mod_tokens, hidden] of mod_dt; y: [batch, n_tokens,
+ * hidden] of y_dt.  Each dtype is VX_F32 or VX_BF16 independently; the
+ * arithmetic is float32.  vx_adaln_modulate(x, .., n_rows, ..) is this call
+ * with batch 1, n_tokens = mod_tokens = n_rows and one dtype throughout.
+ * y == x is allowed when x_dt == y_dt; no other overlap with y is.
+ * Errors: VX_ERR_NULL; VX_ERR_INVALID (batch or n_tokens < 0, hidden <= 0,
+ * mod_tokens neither n_tokens nor 1, eps < 0 or not finite, a bad dtype,
+ * overlaps, y == x with different dtypes); VX_ERR_UNSUPPORTED (hidden not a
+ * multiple of 8 and at most 8192; when all three dtypes are f32, a multiple
+ * of 4 and at most 4096: a row is held in registers); VX_ERR_ALIGN.
+ * batch * n_tokens == 0 launches nothing.
+ */
+int vx_adaln_modulate_ex(const void* x, const void* shift, const void* scale, void* y,
+                         int64_t batch, int64_t n_tokens, int64_t hidden, int64_t mod_tokens,
+                         float eps, int x_dt, int mod_dt, int y_dt, void* hip_stream);
 
 /*
  * 3D RoPE on Q and K, in place (vidax paper §2 "3D RoPE, 3D VAEs, and flash

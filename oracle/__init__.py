@@ -9,6 +9,7 @@ nothing from the package, and the package imports nothing from here.
 Each function writes out the plain definition of what the step computes:
 
 * ``adaln.adaln_modulate``   per-token AdaLN modulation (two-pass LayerNorm)
+* ``adaln.adaln_modulate_per_sample``  one modulation row per sample
 * ``rope3d.rope3d_apply``    3D RoPE as complex multiplication per band
 * ``attention.attention``    naive softmax(Q K^T * scale) V, whole score row
 * ``attention.attention_rope`` RoPE on Q and K, then attention
@@ -28,11 +29,11 @@ convention (band order, pairing, per-band frequencies) is a reading of the
 pages, which give no formula: against any particular model family the RoPE
 convention is parity unpinned; the invariants pin everything else.
 """
-from .adaln import adaln_modulate, layer_norm
+from .adaln import adaln_modulate, adaln_modulate_per_sample, layer_norm
 from .rope3d import token_positions, rope_angles, rope3d_apply
 from .attention import attention, attention_rope, merge_lse, softmax_rows
 
 __all__ = [
-    "adaln_modulate", "layer_norm", "token_positions", "rope_angles",
+    "adaln_modulate", "adaln_modulate_per_sample", "layer_norm", "token_positions", "rope_angles",
     "rope3d_apply", "attention", "attention_rope", "merge_lse", "softmax_rows",
 ]

@@ -8,6 +8,13 @@ weights, bound its memory.  The vidax blog post "Weight offloading: trading
 bandwidth for memory", section "A14B (Wan2.2)", adds that this per-token
 modulation tensor alone is several GB at high resolution.
 
+Wan2.1 (same paper, §3.1 and Table 1) instead modulates every token of a
+sample with one scale and shift row; ``adaln_modulate_per_sample`` writes
+that form out.  Which dtype each tensor is stored in (bf16 or fp32: §3.2
+"Weight import, precision, and verification" keeps Wan2.1's residual stream
+and LTX-2.5's AdaLN tables in fp32) changes only the input values the
+oracle is handed, never its fp64 arithmetic.
+
 Readings where the pages are silent:
 * modulation form ``LN(x) * (1 + scale) + shift`` (so zero modulation is a
   plain LayerNorm);
@@ -37,3 +44,15 @@ def adaln_modulate(x, shift, scale, eps: float = 1e-6) -> np.ndarray:
     shift = np.asarray(shift, dtype=np.float64)
     scale = np.asarray(scale, dtype=np.float64)
     return layer_norm(x, eps) * (1.0 + scale) + shift
+
+
+def adaln_modulate_per_sample(x, shift, scale, eps: float = 1e-6) -> np.ndarray:
+    """y[b, n, :] = LN(x[b, n, :]) * (1 + scale[b, :]) + shift[b, :], in float64.
+
+    ``x`` is [B, N, D]; ``shift`` and ``scale`` are [B, D], one row per
+    sample, the same for all N tokens of that sample.
+    """
+    ln = layer_norm(x, eps)                                 # [B, N, D]
+    shift = np.asarray(shift, dtype=np.float64)[:, None, :]
+    scale = np.asarray(scale, dtype=np.float64)[:, None, :]
+    return ln * (1.0 + scale) + shift

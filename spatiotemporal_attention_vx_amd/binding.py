@@ -16,7 +16,7 @@ from . import build as _build
 VX_F32, VX_BF16 = 0, 1
 STATUS = {0: "VX_OK", 1: "VX_ERR_NULL", 2: "VX_ERR_INVALID", 3: "VX_ERR_UNSUPPORTED",
           4: "VX_ERR_ALIGN", 5: "VX_ERR_HIP"}
-EXPORTS = ("vx_adaln_modulate", "vx_rope3d_apply", "vx_flash_attn_fwd", "vx_flash_attn_fwd_kv",
+EXPORTS = ("vx_adaln_modulate", "vx_adaln_modulate_ex", "vx_rope3d_apply", "vx_flash_attn_fwd", "vx_flash_attn_fwd_kv",
            "vx_attn_merge2", "vx_last_error", "vx_version")
 
 
@@ -53,6 +53,9 @@ def load(path: str | None = None) -> ctypes.CDLL:
     vp, i64 = ctypes.c_void_p, ctypes.c_int64
     lib.vx_adaln_modulate.argtypes = [vp, vp, vp, vp, i64, i64, ctypes.c_float, ctypes.c_int, vp]
     lib.vx_adaln_modulate.restype = ctypes.c_int
+    lib.vx_adaln_modulate_ex.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_float,
+                                         ctypes.c_int, ctypes.c_int, ctypes.c_int, vp]
+    lib.vx_adaln_modulate_ex.restype = ctypes.c_int
     lib.vx_rope3d_apply.argtypes = [vp, vp, i64, i64, i64, i64, ctypes.POINTER(RopeDesc),
                                     ctypes.c_int, vp]
     lib.vx_rope3d_apply.restype = ctypes.c_int
@@ -125,6 +128,27 @@ def adaln_modulate(x, shift, scale, y, eps: float = 1e-6, stream=None):
     rows = x.numel() // hidden if hidden else 0
     _check(load().vx_adaln_modulate(_ptr(x), _ptr(shift), _ptr(scale), _ptr(y), rows, hidden,
                                     eps, _dtype_code(x), _stream(stream)))
+    return y
+
+
+def adaln_modulate_ex(x, shift, scale, y, eps: float = 1e-6, stream=None):
+    """y = LN(x) * (1 + scale) + shift with x, y [B, N, D] and tables [B, N, D]
+    (per token) or [B, 1, D] (per sample); each tensor bf16 or float32."""
+    if x.dim() != 3:
+        raise ValueError(f"x must be [batch, tokens, hidden], got {tuple(x.shape)}")
+    b, n, d = x.shape
+    for name, t in (("x", x), ("shift", shift), ("scale", scale), ("y", y)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous GPU tensor")
+    if tuple(y.shape) != (b, n, d):
+        raise ValueError(f"y is {tuple(y.shape)}, expected {(b, n, d)}")
+    if shift.shape != scale.shape or shift.dtype != scale.dtype:
+        raise ValueError("shift and scale must have the same shape and dtype")
+    if shift.dim() != 3 or shift.shape[0] != b or shift.shape[2] != d or shift.shape[1] not in (1, n):
+        raise ValueError(f"tables are {tuple(shift.shape)}, expected {(b, n, d)} or {(b, 1, d)}")
+    _check(load().vx_adaln_modulate_ex(_ptr(x), _ptr(shift), _ptr(scale), _ptr(y), b, n, d,
+                                       shift.shape[1], eps, _dtype_code(x), _dtype_code(shift),
+                                       _dtype_code(y), _stream(stream)))
     return y
 
 

@@ -1,0 +1,14 @@
+// Per-sample AdaLN modulation (one shift/scale row per sample, broadcast
+// over that sample's tokens): instantiations and launch (the kernel and its
+// statistics are described in adaln_kernel.h).
+#include "adaln_kernel.h"
+
+namespace vx {
+
+hipError_t launch_adaln_per_sample(const void* x, const void* shift, const void* scale, void* y,
+                                   int64_t rows, int64_t n_tokens, int64_t hidden, float eps,
+                                   bool xb, bool mb, bool yb, hipStream_t st) {
+    return adaln_dispatch<true>(x, shift, scale, y, rows, n_tokens, hidden, eps, xb, mb, yb, st);
+}
+
+}  // namespace vx

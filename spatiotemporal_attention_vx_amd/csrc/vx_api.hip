@@ -13,8 +13,12 @@
 #include "vx_device.h"
 
 namespace vx {
-hipError_t launch_adaln(const void* x, const void* shift, const void* scale, void* y,
-                        int64_t rows, int64_t hidden, float eps, bool bf16, hipStream_t st);
+hipError_t launch_adaln_per_token(const void* x, const void* shift, const void* scale, void* y,
+                                  int64_t rows, int64_t hidden, float eps, bool xb, bool mb,
+                                  bool yb, hipStream_t st);
+hipError_t launch_adaln_per_sample(const void* x, const void* shift, const void* scale, void* y,
+                                   int64_t rows, int64_t n_tokens, int64_t hidden, float eps,
+                                   bool xb, bool mb, bool yb, hipStream_t st);
 hipError_t launch_rope3d(void* q, void* k, int64_t batch, int64_t n_tokens, int64_t heads,
                          int64_t head_dim, const RopeArgs& r, bool bf16, hipStream_t st);
 hipError_t launch_flash_attn(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -101,6 +105,55 @@ int launched(hipError_t e, const char* what) {
     return ok();
 }
 
+// Checks shared by the two AdaLN entry points.  Rows are batch * n_tokens;
+// the tables hold mod_tokens rows per batch entry (n_tokens: per token; 1:
+// per sample).
+int adaln(const char* fn, const void* x, const void* shift, const void* scale, void* y,
+          int64_t batch, int64_t n_tokens, int64_t hidden, int64_t mod_tokens, float eps,
+          int x_dt, int mod_dt, int y_dt, void* hip_stream) {
+    if (!x || !shift || !scale || !y) return fail(VX_ERR_NULL, "%s: NULL tensor", fn);
+    for (int dt : {x_dt, mod_dt, y_dt})
+        if (int e = check_dtype(fn, dt)) return e;
+    if (batch < 0 || n_tokens < 0 || hidden <= 0)
+        return fail(VX_ERR_INVALID, "%s: batch %lld, n_tokens %lld, hidden %lld", fn,
+                    (long long)batch, (long long)n_tokens, (long long)hidden);
+    if (mod_tokens != n_tokens && mod_tokens != 1)
+        return fail(VX_ERR_INVALID, "%s: mod_tokens %lld must be n_tokens (%lld) or 1", fn,
+                    (long long)mod_tokens, (long long)n_tokens);
+    if (!std::isfinite(eps) || eps < 0.f)
+        return fail(VX_ERR_INVALID, "%s: eps %g must be finite and >= 0", fn, (double)eps);
+    const bool xb = x_dt == VX_BF16, mb = mod_dt == VX_BF16, yb = y_dt == VX_BF16;
+    // A row lives in registers, at most 16 groups of 8 elements per lane (of
+    // 4 when every tensor is f32).
+    const int64_t group = (xb || mb || yb) ? 8 : 4, max_hidden = 64 * 16 * group;
+    if (hidden % group != 0 || hidden > max_hidden)
+        return fail(VX_ERR_UNSUPPORTED, "%s: hidden %lld must be a multiple of %lld and <= %lld",
+                    fn, (long long)hidden, (long long)group, (long long)max_hidden);
+    if (!aligned16(x) || !aligned16(shift) || !aligned16(scale) || !aligned16(y))
+        return fail(VX_ERR_ALIGN, "%s: tensors must be 16-byte aligned", fn);
+    int64_t rows, xbytes, mbytes, ybytes;
+    if (!mul_ok(rows, {batch, n_tokens}) || !mul_ok(xbytes, {rows, hidden, xb ? 2 : 4}) ||
+        !mul_ok(mbytes, {batch, mod_tokens, hidden, mb ? 2 : 4}) ||
+        !mul_ok(ybytes, {rows, hidden, yb ? 2 : 4}) || (rows + 3) / 4 > INT32_MAX)
+        return fail(VX_ERR_INVALID, "%s: size overflow", fn);
+    if (y == x) {
+        if (x_dt != y_dt)
+            return fail(VX_ERR_INVALID, "%s: y == x needs the same dtype for both", fn);
+        if (overlaps(y, ybytes, shift, mbytes) || overlaps(y, ybytes, scale, mbytes))
+            return fail(VX_ERR_INVALID, "%s: y overlaps shift or scale", fn);
+    } else if (overlaps(y, ybytes, x, xbytes) || overlaps(y, ybytes, shift, mbytes) ||
+               overlaps(y, ybytes, scale, mbytes)) {
+        return fail(VX_ERR_INVALID, "%s: y overlaps an input (only y == x is allowed)", fn);
+    }
+    if (rows == 0) return ok();
+    const hipStream_t st = (hipStream_t)hip_stream;
+    const hipError_t e = (mod_tokens == n_tokens)
+        ? vx::launch_adaln_per_token(x, shift, scale, y, rows, hidden, eps, xb, mb, yb, st)
+        : vx::launch_adaln_per_sample(x, shift, scale, y, rows, n_tokens, hidden, eps, xb, mb,
+                                      yb, st);
+    return launched(e, fn);
+}
+
 // Checks shared by the two attention entry points; nq == nk for the
 // self-attention one.
 int flash_attn(const char* fn, const void* q, const void* k, const void* v, void* o, float* lse,
@@ -146,32 +199,15 @@ extern "C" {
 
 int vx_adaln_modulate(const void* x, const void* shift, const void* scale, void* y,
                       int64_t n_rows, int64_t hidden, float eps, int dt, void* hip_stream) {
-    if (!x || !shift || !scale || !y) return fail(VX_ERR_NULL, "vx_adaln_modulate: NULL tensor");
-    if (int e = check_dtype("vx_adaln_modulate", dt)) return e;
-    if (n_rows < 0 || hidden <= 0)
-        return fail(VX_ERR_INVALID, "vx_adaln_modulate: n_rows %lld, hidden %lld", (long long)n_rows,
-                    (long long)hidden);
-    if (!std::isfinite(eps) || eps < 0.f)
-        return fail(VX_ERR_INVALID, "vx_adaln_modulate: eps %g must be finite and >= 0", (double)eps);
-    const bool bf16 = dt == VX_BF16;
-    const int64_t epc = bf16 ? 8 : 4, max_hidden = bf16 ? 8192 : 4096, esz = bf16 ? 2 : 4;
-    if (hidden % epc != 0 || hidden > max_hidden)
-        return fail(VX_ERR_UNSUPPORTED, "vx_adaln_modulate: hidden %lld must be a multiple of %lld and <= %lld",
-                    (long long)hidden, (long long)epc, (long long)max_hidden);
-    if (!aligned16(x) || !aligned16(shift) || !aligned16(scale) || !aligned16(y))
-        return fail(VX_ERR_ALIGN, "vx_adaln_modulate: tensors must be 16-byte aligned");
-    int64_t bytes;
-    if (!mul_ok(bytes, {n_rows, hidden, esz}) || (n_rows + 3) / 4 > INT32_MAX)
-        return fail(VX_ERR_INVALID, "vx_adaln_modulate: size overflow");
-    if (y != x && (overlaps(y, bytes, x, bytes) || overlaps(y, bytes, shift, bytes) ||
-                   overlaps(y, bytes, scale, bytes)))
-        return fail(VX_ERR_INVALID, "vx_adaln_modulate: y overlaps an input (only y == x is allowed)");
-    if (y == x && (overlaps(y, bytes, shift, bytes) || overlaps(y, bytes, scale, bytes)))
-        return fail(VX_ERR_INVALID, "vx_adaln_modulate: y overlaps shift or scale");
-    if (n_rows == 0) return ok();
-    return launched(vx::launch_adaln(x, shift, scale, y, n_rows, hidden, eps, bf16,
-                                     (hipStream_t)hip_stream),
-                    "vx_adaln_modulate");
+    return adaln("vx_adaln_modulate", x, shift, scale, y, 1, n_rows, hidden, n_rows, eps, dt, dt,
+                 dt, hip_stream);
+}
+
+int vx_adaln_modulate_ex(const void* x, const void* shift, const void* scale, void* y,
+                         int64_t batch, int64_t n_tokens, int64_t hidden, int64_t mod_tokens,
+                         float eps, int x_dt, int mod_dt, int y_dt, void* hip_stream) {
+    return adaln("vx_adaln_modulate_ex", x, shift, scale, y, batch, n_tokens, hidden, mod_tokens,
+                 eps, x_dt, mod_dt, y_dt, hip_stream);
 }
 
 int vx_rope3d_apply(void* q, void* k, int64_t batch, int64_t n_tokens, int64_t heads,

@@ -139,6 +139,23 @@ def adaln_inputs(wl, seed: int = 0):
                  for t, std in ((T_X, 1.0), (T_SHIFT, 0.1), (T_SCALE, 0.1)))
 
 
+def adaln_inputs_ex(wl, x_dtype: str, mod_dtype: str, per_sample: bool, seed: int = 0):
+    """AdaLN inputs with per-tensor storage types and optional per-sample tables.
+
+    x ~ N(0,1) as [batch, rows, width] in ``x_dtype``; shift, scale ~
+    N(0,0.1) in ``mod_dtype`` as [batch, rows, width], or [batch, 1, width]
+    when ``per_sample`` (rows and width as for ``adaln_inputs``).  The x
+    draw is the same as ``adaln_inputs``'s, before its storage rounding.
+    """
+    rows, width, b = wl.adaln_rows, wl.adaln_hidden, wl.batch
+    x = normal_rows(seed, wl.config_id, T_X, rows * b, width, 1.0, None, x_dtype)
+    mrows = b if per_sample else rows * b
+    tabs = tuple(normal_rows(seed, wl.config_id, t, mrows, width, 0.1, None, mod_dtype)
+                 for t in (T_SHIFT, T_SCALE))
+    mshape = (b, 1 if per_sample else rows, width)
+    return (x.reshape(b, rows, width),) + tuple(t.reshape(mshape) for t in tabs)
+
+
 def sample_rows(wl, seed: int = 0, count: int = 0) -> np.ndarray:
     """Sorted query rows the oracle checks on a large workload.
 

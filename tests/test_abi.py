@@ -85,6 +85,42 @@ def test_adaln_rejects(args, code):
 
 
 @host_only
+@pytest.mark.parametrize("ptrs,b,n,d,m,dts,code", [
+    ((None, A + MB, A + 2 * MB, A + 3 * MB), 2, 4, 64, 4, (1, 1, 1), NULL),
+    ((A, A + MB, A + 2 * MB, A + 3 * MB), -1, 4, 64, 4, (1, 1, 1), INVALID),
+    ((A, A + MB, A + 2 * MB, A + 3 * MB), 2, 4, 64, 2, (1, 1, 1), INVALID),      # mod_tokens
+    ((A, A + MB, A + 2 * MB, A + 3 * MB), 2, 4, 64, 4, (1, 5, 1), INVALID),      # dtype
+    ((A, A + MB, A + 2 * MB, A), 2, 4, 64, 4, (0, 1, 1), INVALID),               # y == x, dtypes differ
+    ((A, A + MB, A + 2 * MB, A + 3 * MB), 2, 4, 12, 4, (0, 1, 0), UNSUPPORTED),  # 12 % 8
+    ((A, A + MB, A + 2 * MB, A + 3 * MB), 2, 4, 8200, 4, (0, 1, 1), UNSUPPORTED),
+    ((A, A + MB, A + 2 * MB, A + 3 * MB), 2, 4, 4100, 4, (0, 0, 0), UNSUPPORTED),
+    ((A, A + MB, A + 2 * MB, A + 3 * MB + 4), 2, 4, 64, 1, (1, 1, 1), ALIGN),
+    ((A, A + MB, A + 2 * MB, A + 256), 2, 4, 64, 1, (1, 1, 1), INVALID),         # y overlaps x
+])
+def test_adaln_ex_rejects(ptrs, b, n, d, m, dts, code):
+    lib = binding.load()
+    assert lib.vx_adaln_modulate_ex(*ptrs, b, n, d, m, 1e-6, *dts, None) == code
+    assert lib.vx_last_error().decode().startswith("vx_adaln_modulate_ex")
+
+
+@host_only
+@pytest.mark.parametrize("b,n,d,m,dts", [
+    (2, 4, 12, 4, (0, 0, 0)),          # all f32: groups of 4
+    (2, 4, 8192, 1, (0, 1, 1)),        # f32 residual at the widest row
+    (0, 4, 64, 4, (1, 1, 1)),          # nothing to do
+])
+def test_adaln_ex_accepts_without_launch_on_empty(b, n, d, m, dts):
+    # Valid calls: only the empty one can run without a GPU.
+    lib = binding.load()
+    if b == 0:
+        assert lib.vx_adaln_modulate_ex(A, A + MB, A + 2 * MB, A + 3 * MB, b, n, d, m, 1e-6,
+                                        *dts, None) == OK
+    else:
+        assert lib.vx_adaln_modulate_ex(A, A + MB, A + 2 * MB, A + 3 * MB, 0, n, d, m, 1e-6,
+                                        *dts, None) == OK
+
+
+@host_only
 def test_adaln_zero_rows_is_a_no_op():
     lib = binding.load()
     assert lib.vx_adaln_modulate(A, A + MB, A + 2 * MB, A + 3 * MB, 0, 64, 1e-6, 1, None) == OK

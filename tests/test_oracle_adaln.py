@@ -94,3 +94,49 @@ def test_tiny_workload_matches_library_path():
     ln = torch.nn.functional.layer_norm(torch.from_numpy(x), (wl.hidden,), eps=wl.eps).numpy()
     np.testing.assert_allclose(oracle.adaln_modulate(x, sh, sc, wl.eps), ln * (1 + sc) + sh,
                                rtol=0, atol=1e-12)
+
+
+# ---- one modulation row per sample (Wan2.1)
+
+def test_per_sample_closed_form():
+    # Rows of +-c: LN gives +-c / sqrt(c^2 + eps) exactly, then sample b's row.
+    g = _rng(7)
+    B, N, D, c, eps = 3, 5, 16, 0.75, 1e-6
+    sign = np.array([1.0, -1.0] * (D // 2))
+    x = np.broadcast_to(sign * c, (B, N, D)).copy()
+    shift, scale = g.normal(0, 0.1, (B, D)), g.normal(0, 0.1, (B, D))
+    y = oracle.adaln_modulate_per_sample(x, shift, scale, eps)
+    expect = sign * c / np.sqrt(c * c + eps) * (1.0 + scale[:, None, :]) + shift[:, None, :]
+    np.testing.assert_allclose(y, np.broadcast_to(expect, (B, N, D)), rtol=0, atol=1e-14)
+
+
+def test_per_sample_zero_tables_is_library_layer_norm():
+    g = _rng(8)
+    x = g.standard_normal((2, 7, 48))
+    z = np.zeros((2, 48))
+    y = oracle.adaln_modulate_per_sample(x, z, z, 1e-5)
+    ref = torch.nn.functional.layer_norm(torch.from_numpy(x), (48,), eps=1e-5).numpy()
+    np.testing.assert_allclose(y, ref, rtol=0, atol=1e-12)
+
+
+def test_per_sample_equals_per_token_with_repeated_rows():
+    g = _rng(9)
+    x = g.standard_normal((3, 6, 40))
+    shift, scale = g.normal(0, 0.1, (3, 40)), g.normal(0, 0.1, (3, 40))
+    rep = lambda t: np.repeat(t[:, None, :], 6, axis=1)
+    np.testing.assert_allclose(oracle.adaln_modulate_per_sample(x, shift, scale),
+                               oracle.adaln_modulate(x, rep(shift), rep(scale)),
+                               rtol=0, atol=1e-15)
+
+
+def test_per_sample_row_reaches_only_its_sample():
+    g = _rng(10)
+    x = g.standard_normal((3, 4, 32))
+    shift, scale = g.normal(0, 0.1, (3, 32)), g.normal(0, 0.1, (3, 32))
+    y1 = oracle.adaln_modulate_per_sample(x, shift, scale)
+    shift2, scale2 = shift.copy(), scale.copy()
+    shift2[1] += 1.0
+    scale2[1] *= -2.0
+    y2 = oracle.adaln_modulate_per_sample(x, shift2, scale2)
+    np.testing.assert_array_equal(y1[[0, 2]], y2[[0, 2]])
+    assert np.abs(y1[1] - y2[1]).min() > 0          # every token of sample 1 moves
