@@ -54,6 +54,8 @@ def parse():
                    help="fused: K rotated by vx_rope3d_apply, Q inside the attention load")
     p.add_argument("--adaln", choices=list(ADALN_MODES), default="token",
                    help="AdaLN variant in the step: table layout and storage types")
+    p.add_argument("--pairing", type=int, choices=[0, 1, 2], default=None,
+                   help="RoPE pairing override (0 adjacent, 1 head halves, 2 band halves)")
     p.add_argument("--cpu-rows", type=int, default=512,
                    help="query rows of the oracle CPU baseline (0 = skip it)")
     p.add_argument("--copy-calibration", action="store_true",
@@ -83,7 +85,7 @@ def measured_traffic(wl):
     return rec["bytes_per_launch"]
 
 
-def cpu_baseline(wl, q, k, v, rows_count):
+def cpu_baseline(wl, q, k, v, rows_count, pairing=0):
     """The oracle, as it stands, on `rows_count` query rows x all heads x all keys."""
     import numpy as np
     import oracle
@@ -96,7 +98,8 @@ def cpu_baseline(wl, q, k, v, rows_count):
     rows = inputs.sample_rows(wl, count=rows_count)
     qv, kv, vv = inputs.values(q[0]), inputs.values(k[0]), inputs.values(v[0])
     t0 = time.perf_counter()
-    oracle.attention_rope(qv, kv, vv, wl.grid, wl.split, wl.theta, wl.n_prefix, rows=rows)
+    oracle.attention_rope(qv, kv, vv, wl.grid, wl.split, wl.theta, wl.n_prefix, rows=rows,
+                          pairing=pairing)
     dt = time.perf_counter() - t0
     flops = 4.0 * rows.size * wl.n_tokens * wl.head_dim * wl.heads
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
@@ -150,7 +153,8 @@ def main():
     adaln_bytes = sum(t.numel() * t.element_size() for t in (tx, tsh, tsc, ty))
     to = torch.empty_like(tq)
     gen_s = time.perf_counter() - t0
-    desc = binding.RopeDesc.of(wl.grid, wl.split, wl.theta, wl.n_prefix)
+    pairing = wl.pairing if args.pairing is None else args.pairing
+    desc = binding.RopeDesc.of(wl.grid, wl.split, wl.theta, wl.n_prefix, pairing)
     fused = args.rope == "fused"
     stream = torch.cuda.current_stream()
 
@@ -235,7 +239,7 @@ def main():
                          + f", {wl.n_tokens} tokens, {wl.heads} heads x {wl.head_dim}, "
                          f"{wl.dtype}, batch {wl.batch}"),
             "tokens": wl.n_tokens, "heads": wl.heads, "head_dim": wl.head_dim,
-            "batch": wl.batch, "rope": args.rope,
+            "batch": wl.batch, "rope": args.rope, "rope_pairing": pairing,
             "step": (f"adaln [{wl.adaln_rows}, {wl.adaln_hidden}] + rope3d + flash attention fwd"
                      + (f"; one GPU's share of sequence parallelism over {wl.sp} GPUs "
                         f"(token shard for adaln, {wl.heads} of {wl.sp * wl.heads} heads "
@@ -256,7 +260,7 @@ def main():
         "input_setup_s": round(gen_s, 2),
     }
     if args.cpu_rows > 0:
-        record["cpu_baseline"] = cpu_baseline(wl, q, k, v, args.cpu_rows)
+        record["cpu_baseline"] = cpu_baseline(wl, q, k, v, args.cpu_rows, pairing)
     print(json.dumps(record), flush=True)
 
 

@@ -60,17 +60,22 @@ typedef enum {
  * outermost and w innermost; video positions are the integer grid indices
  * (t, h, w), restarting at 0 after the prefix.  The head dimension is split
  * into contiguous bands [t | h | w] of widths d_t, d_h, d_w (each even,
- * d_t + d_h + d_w == head_dim).  Pair j of band a (elements 2j, 2j+1 of the
- * band) turns by angle pos_a * theta^(-2j / d_a): (x0, x1) ->
- * (x0 cos - x1 sin, x0 sin + x1 cos).  Text tokens are left unchanged.
- * pairing must be 0 (adjacent pairs); other values are reserved.
+ * d_t + d_h + d_w == head_dim).  Pair j of band a turns by angle
+ * pos_a * theta^(-2j / d_a): (x0, x1) -> (x0 cos - x1 sin, x0 sin + x1 cos);
+ * the angles of all bands, listed t then h then w, are the head's d/2
+ * angles.  Which elements form a pair is the family's convention (the
+ * pages stress that conventions differ per family), given by pairing:
+ *   0  adjacent: elements 2j, 2j+1 of the band;
+ *   1  halves of the head: the k-th angle turns elements k and k + d/2;
+ *   2  halves of each band: elements j and j + d_a/2 of the band.
+ * Text tokens are left unchanged.
  */
 typedef struct {
     int32_t T, H, W;       /* latent token grid                              */
     int32_t n_prefix;      /* leading unrotated tokens; 0 if none            */
     int32_t d_t, d_h, d_w; /* band widths                                    */
     float theta;           /* frequency base, finite and > 0 (10000 here)    */
-    int32_t pairing;       /* 0 = adjacent pairs (2i, 2i+1)                  */
+    int32_t pairing;       /* 0 adjacent, 1 head halves, 2 band halves        */
 } vx_rope3d_desc;
 
 /*
@@ -130,7 +135,7 @@ int vx_adaln_modulate_ex(const void* x, const void* shift, const void* scale, vo
  * angles apply to every head and batch entry.  V is never rotated.
  * Errors: VX_ERR_NULL (q and k NULL, or rope NULL); VX_ERR_INVALID (sizes
  * <= 0, T*H*W + n_prefix != n_tokens, grid or prefix negative, odd or
- * mis-summed bands, theta <= 0 or not finite, pairing != 0, q == k);
+ * mis-summed bands, theta <= 0 or not finite, pairing not 0, 1 or 2, q == k);
  * VX_ERR_UNSUPPORTED (head_dim not a multiple of 8, or > 256); VX_ERR_ALIGN.
  */
 int vx_rope3d_apply(void* q, void* k, int64_t batch, int64_t n_tokens, int64_t heads,

@@ -90,7 +90,7 @@ def merge_lse(o_a, lse_a, o_b, lse_b):
 
 
 def attention_rope(q, k, v, grid, split, theta=10000.0, n_prefix=0, scale=0.0,
-                   rows=None):
+                   rows=None, pairing=0):
     """RoPE on Q and K, then attention; one head at a time.
 
     Arguments as in ``attention``; returns (o [R, H, d], lse [H, R]).
@@ -100,8 +100,9 @@ def attention_rope(q, k, v, grid, split, theta=10000.0, n_prefix=0, scale=0.0,
     o = np.empty((rows.size, heads, d), dtype=np.float64)
     lse = np.empty((heads, rows.size), dtype=np.float64)
     for h in range(heads):
-        kr = rope3d_apply(k[:, h:h + 1, :], grid, split, theta, n_prefix)
-        qr = rope3d_apply(q[rows, h:h + 1, :], grid, split, theta, n_prefix, tokens=rows)
+        kr = rope3d_apply(k[:, h:h + 1, :], grid, split, theta, n_prefix, pairing=pairing)
+        qr = rope3d_apply(q[rows, h:h + 1, :], grid, split, theta, n_prefix, tokens=rows,
+                          pairing=pairing)
         # attention() indexes q by token, so place the rotated rows at 0..R-1
         oh, lh = attention(qr, kr, v[:, h:h + 1, :], scale)
         o[:, h:h + 1, :] = oh

@@ -15,8 +15,14 @@ The pages print no formula.  Readings taken here (one convention, stated):
   positions are the integer grid indices;
 * the head dimension is split into contiguous bands [t | h | w] of widths
   (d_t, d_h, d_w);
-* within a band of width d_a, pair j (elements 2j, 2j+1 of the band) turns
-  by angle pos_a * theta ** (-2 j / d_a);
+* within a band of width d_a, pair j turns by angle
+  pos_a * theta ** (-2 j / d_a); the angles of all bands, listed t, h, w,
+  form the head's d/2 angles;
+* which two elements form pair j depends on the family's convention
+  (``pairing``): 0, adjacent elements 2j, 2j+1 of the band; 1, the head
+  split in halves, the k-th angle of the [t | h | w] list turning elements
+  k and k + d/2 of the head; 2, each band split in halves, elements j and
+  j + d_a/2 of the band;
 * a pair (a, b) read as the complex number a + i b is multiplied by
   exp(i * angle);
 * the same angles apply to every head and to Q and K; V is not rotated;
@@ -45,12 +51,32 @@ def rope_angles(grid, split, theta: float = 10000.0, n_prefix: int = 0) -> np.nd
     return np.concatenate(cols, axis=1)
 
 
+def pair_elements(split, pairing: int = 0):
+    """(first, second) element indices of the head's d/2 pairs, in angle order."""
+    d = int(sum(split))
+    k = np.arange(d // 2)
+    if pairing == 0:
+        return 2 * k, 2 * k + 1
+    if pairing == 1:
+        return k, k + d // 2
+    if pairing == 2:
+        firsts, seconds, start = [], [], 0
+        for width in split:
+            j = np.arange(width // 2)
+            firsts.append(start + j)
+            seconds.append(start + j + width // 2)
+            start += width
+        return np.concatenate(firsts), np.concatenate(seconds)
+    raise ValueError(f"unknown pairing {pairing}")
+
+
 def rope3d_apply(x, grid, split, theta: float = 10000.0, n_prefix: int = 0,
-                 tokens=None) -> np.ndarray:
+                 tokens=None, pairing: int = 0) -> np.ndarray:
     """Rotate x of shape [N, heads, head_dim]; returns a float64 copy.
 
     ``tokens`` (optional) lists the token indices the rows of x hold; by
-    default x holds all N = n_prefix + T*H*W tokens in order.
+    default x holds all N = n_prefix + T*H*W tokens in order.  ``pairing``
+    picks which elements form each rotated pair (see the module notes).
     """
     x = np.array(x, dtype=np.float64, copy=True)
     d = x.shape[-1]
@@ -68,9 +94,10 @@ def rope3d_apply(x, grid, split, theta: float = 10000.0, n_prefix: int = 0,
     video = tokens >= n_prefix
     ang = rope_angles(grid, split, theta, n_prefix)[tokens[video] - n_prefix]
     rot = np.exp(1j * ang)[:, None, :]                         # [Nv, 1, d/2]
+    first, second = pair_elements(split, pairing)
     vid = x[video]
-    z = (vid[..., 0::2] + 1j * vid[..., 1::2]) * rot
-    vid[..., 0::2] = z.real
-    vid[..., 1::2] = z.imag
+    z = (vid[..., first] + 1j * vid[..., second]) * rot
+    vid[..., first] = z.real
+    vid[..., second] = z.imag
     x[video] = vid
     return x

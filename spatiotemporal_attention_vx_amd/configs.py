@@ -30,6 +30,7 @@ class Workload:
     batch: int = 1
     oracle_rows: int = 0    # 0: the oracle checks every row; else a sample
     sp: int = 1             # sequence-parallel degree this is one GPU's share of
+    pairing: int = 0        # RoPE pairs: 0 adjacent, 1 halves of the head, 2 halves of each band
 
     @property
     def adaln_rows(self) -> int:
@@ -105,13 +106,25 @@ SP_WORKLOADS = {
 }
 
 
+# Model-family shapes beyond the five grids.  CogVideoX1.5 patches two
+# latent frames into one token (temporal patch 2), so its 1360x768 / 81-frame
+# video is an 11 x 48 x 85 token grid; with its 226 text tokens that is
+# 45,106 tokens, the "about 45k" joint-attention length the vidax paper
+# reports for it (§4, Table 3, and the agihunt.info summary).  48 heads x
+# 64, RoPE bands 16/24/24 as for the mixed workload.
+FAMILY_WORKLOADS = {
+    "cogvx15": Workload("cogvx15", 10, (11, 48, 85), 226, 48, 64, "bf16", (16, 24, 24),
+                        oracle_rows=256),
+}
+
+
 def get(name: str) -> Workload:
-    """A workload by name: one of WORKLOADS or SP_WORKLOADS."""
-    if name in WORKLOADS:
-        return WORKLOADS[name]
-    if name in SP_WORKLOADS:
-        return SP_WORKLOADS[name]
-    raise KeyError(f"unknown workload {name!r}; known: {sorted(WORKLOADS) + sorted(SP_WORKLOADS)}")
+    """A workload by name: one of WORKLOADS, SP_WORKLOADS or FAMILY_WORKLOADS."""
+    for table in (WORKLOADS, SP_WORKLOADS, FAMILY_WORKLOADS):
+        if name in table:
+            return table[name]
+    known = sorted(WORKLOADS) + sorted(SP_WORKLOADS) + sorted(FAMILY_WORKLOADS)
+    raise KeyError(f"unknown workload {name!r}; known: {known}")
 
 
 # The measured workload: 75,600 tokens, 40 heads x 128.

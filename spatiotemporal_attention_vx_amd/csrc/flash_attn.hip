@@ -178,7 +178,7 @@ __device__ __forceinline__ void load_q_fragment(const FaArgs& a, const uint16_t*
         uint4 w = {0u, 0u, 0u, 0u};
         if (qi < a.nq) w = *(const uint4*)(qb + qi * a.row_stride + ks * 16 + g * 8);
         uint32_t u[4] = {w.x, w.y, w.z, w.w};
-        if (a.use_rope && qi < a.nq) {
+        if (a.use_rope && qi < a.nq && a.rope.pairing == 0) {
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
                 const int pair = (ks * 16 + g * 8) / 2 + m;
@@ -191,6 +191,29 @@ __device__ __forceinline__ void load_q_fragment(const FaArgs& a, const uint16_t*
                     u[m] = pack_bf16x2(x0, x1);
                 }
             }
+        } else if (a.use_rope && qi < a.nq) {
+            // half-split pairings: the partner element lies elsewhere in the
+            // row and is read from memory (once per workgroup, before the
+            // key loop)
+            const uint16_t* qrow = qb + qi * a.row_stride;
+            float out[8];
+#pragma unroll
+            for (int m = 0; m < 8; ++m) {
+                const int e = ks * 16 + g * 8 + m;
+                const float xe = (m & 1) ? bf16_hi(u[m >> 1]) : bf16_lo(u[m >> 1]);
+                int pair, partner, pos, j, width;
+                bool second;
+                rope_elem_pair(a.rope, e, &pair, &partner, &second);
+                out[m] = xe;
+                if (rope_pair_geometry(a.rope, qi, pair, &pos, &j, &width)) {
+                    float c, s;
+                    rope_cos_sin(a.rope, pos, j, width, &c, &s);
+                    const float xp = __uint_as_float((uint32_t)qrow[partner] << 16);
+                    out[m] = rope_rotate_elem(xe, xp, second, c, s);
+                }
+            }
+#pragma unroll
+            for (int m = 0; m < 4; ++m) u[m] = pack_bf16x2(out[2 * m], out[2 * m + 1]);
         }
 #pragma unroll
         for (int m = 0; m < 4; ++m)
@@ -886,7 +909,7 @@ void fa_fwd_f32_kernel(FaArgs a) {
         qv[e] = qi < nq ? qb[qi * a.row_stride + part * 32 + e] : 0.f;
         acc[e] = 0.f;
     }
-    if (a.use_rope && qi < nq) {
+    if (a.use_rope && qi < nq && a.rope.pairing == 0) {
 #pragma unroll
         for (int m = 0; m < 16; ++m) {
             int pos, j, width;
@@ -896,6 +919,24 @@ void fa_fwd_f32_kernel(FaArgs a) {
                 rope_rotate(qv[2 * m], qv[2 * m + 1], c, s);
             }
         }
+    } else if (a.use_rope && qi < nq) {
+        // half-split pairings: partners are read from the row in memory
+        const float* qrow = qb + qi * a.row_stride;
+        float out[32];
+#pragma unroll
+        for (int e = 0; e < 32; ++e) {
+            int pair, partner, pos, j, width;
+            bool second;
+            rope_elem_pair(a.rope, part * 32 + e, &pair, &partner, &second);
+            out[e] = qv[e];
+            if (rope_pair_geometry(a.rope, qi, pair, &pos, &j, &width)) {
+                float c, s;
+                rope_cos_sin(a.rope, pos, j, width, &c, &s);
+                out[e] = rope_rotate_elem(qv[e], qrow[partner], second, c, s);
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < 32; ++e) qv[e] = out[e];
     }
 
     float m_run = -__builtin_inff(), l_run = 0.f;
@@ -970,7 +1011,7 @@ hipError_t launch_flash_attn(const void* q, const void* k, const void* v, void* 
     a.scale_log2 = scale * 1.4426950408889634f;
     a.use_rope = rope != nullptr;
     if (rope) a.rope = *rope;
-    else a.rope = RopeArgs{1, 1, 1, 0, 0, 0, 0, 1.f};
+    else a.rope = RopeArgs{1, 1, 1, 0, 0, 0, 0, 1.f, 0};
 
     const int rows_per_wg = flash_attn_rows_per_workgroup(bf16, head_dim);
     a.n_qtiles = (int)((nq + rows_per_wg - 1) / rows_per_wg);

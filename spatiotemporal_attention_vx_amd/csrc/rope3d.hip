@@ -11,7 +11,11 @@
 // head_dim/2 angles of each token into LDS (angles are shared by every head
 // and by Q and K, so they cost one evaluation per token and pair), then
 // streams the 16-byte chunks of the tokens' Q and K rows, consecutive lanes
-// on consecutive chunks.
+// on consecutive chunks.  With adjacent pairs (pairing 0) both elements of
+// a pair sit in one chunk.  With the half-split pairings (1: halves of the
+// head, 2: halves of each band) a pair spans chunks, so each head row is
+// staged through LDS first and every lane reads its elements' partners
+// there.
 #include "vx_device.h"
 
 namespace vx {
@@ -84,10 +88,88 @@ void rope3d_kernel(uint4* q, uint4* k, int64_t rows, int64_t n_tokens, int heads
     }
 }
 
+// Half-split pairings.  The (token, tensor, head) rows of the workgroup's
+// tokens are taken 256 / (head_dim / EPC) at a time: one thread per 16-byte
+// chunk loads it, keeps its values and writes them to LDS; after a barrier
+// each thread rotates its elements with their partners from LDS and stores
+// its chunk back.
+template <bool BF16>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256)))
+void rope3d_split_kernel(uint4* q, uint4* k, int64_t rows, int64_t n_tokens, int heads,
+                         int head_dim, RopeArgs r) {
+    constexpr int EPC = BF16 ? 8 : 4;
+    __shared__ f32x2_t cs[ROPE_TPB * ROPE_MAX_HALF];
+    __shared__ float xs[256 * EPC];      // staged head rows
+    __shared__ int rotate[ROPE_TPB];     // token exists and is not text
+    const int half = head_dim >> 1;
+    const int64_t row0 = (int64_t)blockIdx.x * ROPE_TPB;
+
+    for (int i = threadIdx.x; i < ROPE_TPB * half; i += 256) {
+        const int tk = i / half, pair = i - tk * half;
+        const int64_t row = row0 + tk;
+        float c = 1.f, s = 0.f;
+        int pos, j, width;
+        if (row < rows && rope_pair_geometry(r, row % n_tokens, pair, &pos, &j, &width))
+            rope_cos_sin(r, pos, j, width, &c, &s);
+        cs[i] = f32x2_t{c, s};
+    }
+    if (threadIdx.x < ROPE_TPB) {
+        const int64_t row = row0 + threadIdx.x;
+        rotate[threadIdx.x] = row < rows && (row % n_tokens) >= r.n_prefix;
+    }
+    __syncthreads();
+
+    const int dpr = head_dim / EPC;              // chunks per head row
+    const int per_iter = 256 / dpr;              // head rows per pass
+    const int slot = threadIdx.x / dpr, c = threadIdx.x - slot * dpr;
+    const int64_t units = (int64_t)ROPE_TPB * 2 * heads;   // (token, tensor, head), head fastest
+    float* const mine = xs + slot * head_dim;
+    for (int64_t u0 = 0; u0 < units; u0 += per_iter) {
+        const int64_t u = u0 + slot;
+        bool live = slot < per_iter && u < units;
+        const int h = live ? (int)(u % heads) : 0, tw = live ? (int)(u / heads) : 0;
+        const int which = tw & 1, tk = tw >> 1;
+        uint4* base = which ? k : q;
+        live = live && base != nullptr && rotate[tk];
+        uint4* p = live ? base + ((row0 + tk) * heads + h) * dpr + c : nullptr;
+        float f[EPC];
+        if (live) {
+            const uint4 v = *p;
+            unpack_chunk<BF16>(u32x4_t{v.x, v.y, v.z, v.w}, f);
+#pragma unroll
+            for (int m = 0; m < EPC; ++m) mine[c * EPC + m] = f[m];
+        }
+        __syncthreads();
+        if (live) {
+            float out[EPC];
+#pragma unroll
+            for (int m = 0; m < EPC; ++m) {
+                int pair, partner;
+                bool second;
+                rope_elem_pair(r, c * EPC + m, &pair, &partner, &second);
+                const f32x2_t e = cs[tk * half + pair];
+                out[m] = rope_rotate_elem(f[m], mine[partner], second, e.x, e.y);
+            }
+            const u32x4_t w = pack_chunk<BF16>(out);
+            *p = uint4{w[0], w[1], w[2], w[3]};
+        }
+        __syncthreads();
+    }
+}
+
 hipError_t launch_rope3d(void* q, void* k, int64_t batch, int64_t n_tokens, int64_t heads,
                          int64_t head_dim, const RopeArgs& r, bool bf16, hipStream_t st) {
     const int64_t rows = batch * n_tokens;
     const int64_t blocks = (rows + ROPE_TPB - 1) / ROPE_TPB;
+    if (r.pairing != 0) {
+        if (bf16)
+            hipLaunchKernelGGL(rope3d_split_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, st,
+                               (uint4*)q, (uint4*)k, rows, n_tokens, (int)heads, (int)head_dim, r);
+        else
+            hipLaunchKernelGGL(rope3d_split_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, st,
+                               (uint4*)q, (uint4*)k, rows, n_tokens, (int)heads, (int)head_dim, r);
+        return hipGetLastError();
+    }
     if (bf16)
         hipLaunchKernelGGL(rope3d_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, st,
                            (uint4*)q, (uint4*)k, rows, n_tokens, (int)heads, (int)head_dim, r);

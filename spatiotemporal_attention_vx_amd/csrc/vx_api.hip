@@ -93,10 +93,11 @@ int check_rope(const char* fn, const vx_rope3d_desc* r, int64_t n_tokens, int64_
     if (!std::isfinite(r->theta) || r->theta <= 0.f)
         return fail(VX_ERR_INVALID, "%s: rope theta %g must be finite and positive", fn,
                     (double)r->theta);
-    if (r->pairing != 0)
-        return fail(VX_ERR_INVALID, "%s: rope pairing %d is reserved (only 0, adjacent pairs)", fn,
-                    r->pairing);
-    *out = vx::RopeArgs{r->T, r->H, r->W, r->n_prefix, r->d_t, r->d_h, r->d_w, r->theta};
+    if (r->pairing < 0 || r->pairing > 2)
+        return fail(VX_ERR_INVALID, "%s: rope pairing %d is not 0 (adjacent), 1 (head halves) "
+                    "or 2 (band halves)", fn, r->pairing);
+    *out = vx::RopeArgs{r->T, r->H, r->W, r->n_prefix, r->d_t, r->d_h, r->d_w, r->theta,
+                        r->pairing};
     return VX_OK;
 }
 

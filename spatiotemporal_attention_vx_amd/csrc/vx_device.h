@@ -57,6 +57,7 @@ struct RopeArgs {
     int32_t n_prefix;
     int32_t d_t, d_h, d_w;
     float theta;
+    int32_t pairing;   // 0 adjacent pairs, 1 halves of the head, 2 halves of each band
 };
 
 // Position along the band that pair `pair` of the head dimension belongs
@@ -75,6 +76,39 @@ __device__ __forceinline__ bool rope_pair_geometry(const RopeArgs& r, int64_t to
     else if (pair < pt + ph) { *pos = h; *j = pair - pt; *width = r.d_h; }
     else { *pos = w; *j = pair - pt - ph; *width = r.d_w; }
     return true;
+}
+
+// Pair of element e of the head dimension under the call's pairing: the
+// pair's index in angle order ([t | h | w] bands, as rope_pair_geometry
+// numbers them), the other element of the pair, and whether e is the
+// pair's second element (the imaginary part of a + i b).
+__device__ __forceinline__ void rope_elem_pair(const RopeArgs& r, int e, int* pair, int* partner,
+                                               bool* second) {
+    if (r.pairing == 0) {            // (2j, 2j + 1)
+        *pair = e >> 1;
+        *second = (e & 1) != 0;
+        *partner = e ^ 1;
+    } else if (r.pairing == 1) {     // (k, k + d/2), k-th angle of the whole list
+        const int half = (r.d_t + r.d_h + r.d_w) >> 1;
+        *second = e >= half;
+        *pair = *second ? e - half : e;
+        *partner = *second ? e - half : e + half;
+    } else {                         // (s_a + j, s_a + j + d_a/2) inside band a
+        int start, width, first_pair;
+        if (e < r.d_t) { start = 0; width = r.d_t; first_pair = 0; }
+        else if (e < r.d_t + r.d_h) { start = r.d_t; width = r.d_h; first_pair = r.d_t >> 1; }
+        else { start = r.d_t + r.d_h; width = r.d_w; first_pair = (r.d_t + r.d_h) >> 1; }
+        const int l = e - start, hw = width >> 1;
+        *second = l >= hw;
+        *pair = first_pair + (*second ? l - hw : l);
+        *partner = *second ? e - hw : e + hw;
+    }
+}
+
+// Element e of a rotated pair from its own value xe and its partner's xp,
+// the same expressions as rope_rotate.
+__device__ __forceinline__ float rope_rotate_elem(float xe, float xp, bool second, float c, float s) {
+    return second ? __builtin_fmaf(xp, s, xe * c) : __builtin_fmaf(xe, c, -xp * s);
 }
 
 // cos and sin of the RoPE angle pos * theta^(-2j/width), evaluated in double

@@ -138,7 +138,8 @@ def test_adaln_zero_rows_is_a_no_op():
     (A, A + MB, 24, 64, _rope(d_t=18), INVALID),               # bands sum != d
     (A, A + MB, 24, 64, _rope(theta=0.0), INVALID),
     (A, A + MB, 24, 64, _rope(theta=float("inf")), INVALID),
-    (A, A + MB, 24, 64, _rope(pairing=1), INVALID),
+    (A, A + MB, 24, 64, _rope(pairing=3), INVALID),
+    (A, A + MB, 24, 64, _rope(pairing=-1), INVALID),
     (A, A + MB, 24, 64, _rope(T=-1), INVALID),
     (A, A + MB, 24, 60, _rope(d_t=12), UNSUPPORTED),
     (A, A + MB, 24, 264, _rope(d_t=216), UNSUPPORTED),

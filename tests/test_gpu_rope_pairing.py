@@ -1,0 +1,140 @@
+"""GPU parity of the half-split 3D-RoPE pairings (halves of the head,
+halves of each band) in vx_rope3d_apply and in the fused Q rotation of
+vx_flash_attn_fwd, and of the CogVideoX1.5 token grid, against the fp64
+oracle."""
+import numpy as np
+import pytest
+
+import oracle
+from _helpers import bits, check, dev, host, say
+from spatiotemporal_attention_vx_amd import binding, configs, inputs
+
+pytestmark = pytest.mark.gpu
+
+LSE_TOL_ROPE = {"f32": 1e-5, "bf16": 1e-2}
+
+
+@pytest.mark.parametrize("pairing", [1, 2])
+@pytest.mark.parametrize("dtype,grid,prefix,heads,d,batch,split", [
+    ("f32", (1, 1, 1), 0, 1, 64, 1, (16, 24, 24)),
+    ("f32", (2, 3, 5), 7, 3, 128, 2, (44, 42, 42)),
+    ("bf16", (2, 3, 5), 7, 3, 128, 2, (44, 42, 42)),
+    ("bf16", (3, 1, 4), 0, 5, 64, 1, (16, 24, 24)),
+    ("bf16", (2, 2, 2), 1, 2, 8, 1, (2, 2, 4)),
+    ("bf16", (2, 4, 3), 0, 1, 256, 3, (64, 96, 96)),
+    ("bf16", (5, 2, 3), 3, 2, 96, 1, (0, 48, 48)),
+    ("bf16", (3, 3, 3), 2, 40, 128, 1, (16, 56, 56)),
+    ("f32", (2, 2, 3), 0, 3, 72, 1, (24, 24, 24)),
+])
+def test_ragged(gpu_lib, pairing, dtype, grid, prefix, heads, d, batch, split):
+    import torch
+    n = prefix + grid[0] * grid[1] * grid[2]
+    say(f"rope pairing={pairing} {dtype} grid={grid} prefix={prefix} heads={heads} d={d} "
+        f"batch={batch} split={split}")
+    g = np.random.default_rng(n * 37 + d + pairing)
+    q = inputs.storage(g.standard_normal((batch, n, heads, d)).astype(np.float32), dtype)
+    k = inputs.storage(g.standard_normal((batch, n, heads, d)).astype(np.float32), dtype)
+    tq, tk = dev(q), dev(k)
+    binding.rope3d_apply(tq, tk, binding.RopeDesc.of(grid, split, 10000.0, prefix, pairing))
+    torch.cuda.synchronize()
+    for src, t, nm in ((q, tq, "q"), (k, tk, "k")):
+        got = host(t)
+        for b in range(batch):
+            ref = oracle.rope3d_apply(inputs.values(src[b]).astype(np.float64), grid, split,
+                                      10000.0, prefix, pairing=pairing)
+            check(got[b], ref, dtype, f"rope p{pairing} {nm}[{b}]")
+        if prefix:
+            np.testing.assert_array_equal(bits(t)[:, :prefix],
+                                          src[:, :prefix].view(np.int16 if dtype == "bf16"
+                                                               else np.int32))
+
+
+def test_only_one_tensor(gpu_lib):
+    """q = NULL rotates k alone (and the reverse) under a half-split pairing."""
+    import torch
+    say("rope pairing=2 one tensor")
+    grid, split = (2, 3, 4), (16, 24, 24)
+    g = np.random.default_rng(71)
+    x = inputs.storage(g.standard_normal((1, 24, 4, 64)).astype(np.float32), "bf16")
+    desc = binding.RopeDesc.of(grid, split, 10000.0, 0, 2)
+    ta, tb = dev(x), dev(x)
+    binding.rope3d_apply(None, ta, desc)
+    binding.rope3d_apply(tb, None, desc)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(bits(ta), bits(tb))
+    ref = oracle.rope3d_apply(inputs.values(x[0]).astype(np.float64), grid, split, pairing=2)
+    check(host(ta)[0], ref, "bf16", "rope k only")
+
+
+@pytest.mark.parametrize("pairing", [1, 2])
+@pytest.mark.parametrize("dtype,d,split", [("bf16", 64, (16, 24, 24)), ("bf16", 128, (44, 42, 42)),
+                                           ("f32", 64, (16, 24, 24)), ("f32", 128, (16, 56, 56))])
+def test_fused_rope_q_matches_separate(gpu_lib, pairing, dtype, d, split):
+    """Rotating Q inside the attention load gives the same bits as rotating
+    it in memory first; both match the oracle's RoPE-then-attention."""
+    import torch
+    say(f"attn fused rope_q pairing={pairing} {dtype} d={d}")
+    grid, prefix = (3, 5, 7), 5
+    n = prefix + 3 * 5 * 7
+    g = np.random.default_rng(90 + d + pairing)
+    q, k, v = (inputs.storage(g.standard_normal((1, n, 2, d)).astype(np.float32), dtype)
+               for _ in range(3))
+    desc = binding.RopeDesc.of(grid, split, 10000.0, prefix, pairing)
+    tq, tk, tv = dev(q), dev(k), dev(v)
+    binding.rope3d_apply(None, tk, desc)
+    o1, l1 = torch.empty_like(tq), torch.empty((1, 2, n), device="cuda")
+    binding.flash_attn_fwd(tq, tk, tv, o1, l1, rope_q=desc)
+    tq2 = dev(q)
+    binding.rope3d_apply(tq2, None, desc)
+    o2, l2 = torch.empty_like(tq), torch.empty((1, 2, n), device="cuda")
+    binding.flash_attn_fwd(tq2, tk, tv, o2, l2)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(bits(o1), bits(o2))
+    np.testing.assert_array_equal(l1.cpu().numpy(), l2.cpu().numpy())
+    ref, rl = oracle.attention_rope(inputs.values(q[0]), inputs.values(k[0]), inputs.values(v[0]),
+                                    grid, split, 10000.0, prefix, pairing=pairing)
+    check(host(o1)[0], ref, dtype, "o")
+    assert np.abs(l1.cpu().numpy()[0] - rl).max() <= LSE_TOL_ROPE[dtype]
+
+
+def _workload_attention(wl, pairing):
+    import torch
+    q, k, v = inputs.attention_inputs(wl)
+    desc = binding.RopeDesc.of(wl.grid, wl.split, wl.theta, wl.n_prefix, pairing)
+    tq, tk, tv = dev(q), dev(k), dev(v)
+    binding.rope3d_apply(None, tk, desc)
+    o = torch.empty_like(tq)
+    lse = torch.empty((1, wl.heads, wl.n_tokens), device="cuda")
+    binding.flash_attn_fwd(tq, tk, tv, o, lse, rope_q=desc)
+    torch.cuda.synchronize()
+    rows = inputs.sample_rows(wl)
+    og, lg = host(o)[0, rows], lse.cpu().numpy()[0][:, rows]
+    del o, lse, tq, tk, tv
+    ref, rl = oracle.attention_rope(inputs.values(q[0]), inputs.values(k[0]), inputs.values(v[0]),
+                                    wl.grid, wl.split, wl.theta, wl.n_prefix, rows=rows,
+                                    pairing=pairing)
+    check(og, ref, wl.dtype, f"attn {wl.name} pairing {pairing}")
+    lse_err = float(np.abs(lg - rl).max())
+    say(f"  lse max abs {lse_err:.3e}")
+    assert lse_err <= LSE_TOL_ROPE[wl.dtype]
+
+
+@pytest.mark.timeout(1200)
+def test_cogvideox15_grid(gpu_lib):
+    """226 text tokens + 11 x 48 x 85 video tokens, 48 heads x 64: RoPE on K,
+    Q rotated in the attention load; 256 seeded rows x every head x every
+    key against the oracle."""
+    wl = configs.FAMILY_WORKLOADS["cogvx15"]
+    say(f"attn workload {wl.name}: N={wl.n_tokens} H={wl.heads} d={wl.head_dim}")
+    assert wl.n_tokens == 45_106
+    _workload_attention(wl, wl.pairing)
+
+
+@pytest.mark.timeout(1200)
+@pytest.mark.parametrize("pairing", [1, 2])
+def test_large_grid_half_split(gpu_lib, pairing):
+    """The 75,600-token grid under each half-split pairing, at one GPU's
+    sequence-parallel share (5 heads) to keep the oracle's work small."""
+    wl = configs.SP_WORKLOADS["large_sp8"]
+    say(f"attn workload {wl.name} pairing={pairing}")
+    _workload_attention(wl, pairing)

@@ -145,3 +145,94 @@ def test_rejects_bad_split():
         oracle.rope3d_apply(np.zeros((48, 1, 64)), GRID, (16, 23, 25))
     with pytest.raises(ValueError):
         oracle.rope3d_apply(np.zeros((48, 1, 64)), GRID, (16, 24, 26))
+
+
+# ---- half-split pairings (pairing 1: halves of the head; 2: halves of each band)
+
+# (token, angle, (first, second) element indices under pairing 1, under pairing 2)
+# for SPLIT (16, 24, 24), head_dim 64, angle list [t: 8 | h: 12 | w: 12]:
+# t pair 1 is angle 1; h pair 3 is angle 8 + 3 = 11; w pair 6 is angle 26.
+HALF_CLOSED = [
+    (16, 1 * 10 ** -0.5, (1, 33), (1, 9)),              # t=1, t band pair 1
+    (8, 2 * 1e-1, (11, 43), (19, 31)),                  # h=2, h band pair 3
+    (3, 3 * 1e-2, (26, 58), (46, 58)),                  # w=3, w band pair 6
+    (3, 3.0, (20, 52), (40, 52)),                       # w=3, w band pair 0
+]
+
+
+@pytest.mark.parametrize("token,angle,p1,p2", HALF_CLOSED)
+@pytest.mark.parametrize("pairing", [1, 2])
+def test_half_split_closed_form(token, angle, p1, p2, pairing):
+    a, b = p1 if pairing == 1 else p2
+    d = sum(SPLIT)
+    for src, expect_a, expect_b in ((a, math.cos(angle), math.sin(angle)),
+                                    (b, -math.sin(angle), math.cos(angle))):
+        x = np.zeros((48, 1, d))
+        x[token, 0, src] = 1.0
+        y = oracle.rope3d_apply(x, GRID, SPLIT, pairing=pairing)
+        expect = np.zeros(d)
+        expect[a], expect[b] = expect_a, expect_b
+        np.testing.assert_allclose(y[token, 0], expect, rtol=0, atol=1e-15)
+
+
+def _to_adjacent(pairing):
+    """Permutation P (written out per convention) with (P x)[2k], (P x)[2k+1] =
+    the k-th pair's first and second elements."""
+    if pairing == 1:
+        first, second = list(range(0, 32)), list(range(32, 64))
+    else:   # bands t: 0..15, h: 16..39, w: 40..63, each split in halves
+        first = list(range(0, 8)) + list(range(16, 28)) + list(range(40, 52))
+        second = list(range(8, 16)) + list(range(28, 40)) + list(range(52, 64))
+    perm = np.empty(64, dtype=np.int64)
+    perm[0::2], perm[1::2] = first, second
+    return perm
+
+
+@pytest.mark.parametrize("pairing", [1, 2])
+def test_half_split_is_adjacent_under_a_permutation(pairing):
+    g = np.random.default_rng(20 + pairing)
+    x = g.standard_normal((48, 2, 64))
+    perm = _to_adjacent(pairing)
+    y = oracle.rope3d_apply(x, GRID, SPLIT, pairing=pairing)
+    y0 = oracle.rope3d_apply(x[..., perm], GRID, SPLIT, pairing=0)
+    back = np.empty_like(y0)
+    back[..., perm] = y0
+    np.testing.assert_allclose(y, back, rtol=0, atol=1e-14)
+
+
+@pytest.mark.parametrize("pairing", [1, 2])
+def test_half_split_invariants(pairing):
+    g = np.random.default_rng(30 + pairing)
+    q, k = g.standard_normal(64), g.standard_normal(64)
+
+    def rot(vec, pos):
+        t, h, w = pos
+        grid = (t + 1, h + 1, w + 1)
+        x = np.zeros((grid[0] * grid[1] * grid[2], 1, 64))
+        idx = t * grid[1] * grid[2] + h * grid[2] + w
+        x[idx, 0] = vec
+        return oracle.rope3d_apply(x, grid, SPLIT, pairing=pairing)[idx, 0]
+
+    # identity at the origin, norm kept, scores depend only on the offset
+    np.testing.assert_array_equal(rot(q, (0, 0, 0)), q)
+    assert abs(np.linalg.norm(rot(q, (2, 1, 3))) - np.linalg.norm(q)) < 1e-12
+    p, pp, delta = (1, 2, 0), (3, 0, 5), (2, 3, 1)
+    s1 = rot(q, p) @ rot(k, pp)
+    s2 = rot(q, tuple(a + b for a, b in zip(p, delta))) @ rot(k, tuple(a + b for a, b in zip(pp, delta)))
+    assert abs(s1 - s2) < 1e-12
+    # text prefix rows stay as they are under every pairing
+    x = g.standard_normal((3 + 48, 1, 64))
+    y = oracle.rope3d_apply(x, GRID, SPLIT, n_prefix=3, pairing=pairing)
+    np.testing.assert_array_equal(y[:3], x[:3])
+
+
+def test_zero_width_band():
+    # a band of width 0 contributes no pairs; the others keep their layout
+    g = np.random.default_rng(40)
+    x = g.standard_normal((48, 1, 48))
+    for pairing in (0, 1, 2):
+        y = oracle.rope3d_apply(x, GRID, (0, 24, 24), pairing=pairing)
+        np.testing.assert_allclose((y ** 2).sum(-1), (x ** 2).sum(-1), rtol=1e-12)
+        # tokens at h = w = 0 (t varies) are not rotated at all
+        for tok in (0, 16, 32):
+            np.testing.assert_array_equal(y[tok], x[tok])
