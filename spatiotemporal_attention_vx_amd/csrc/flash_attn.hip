@@ -169,56 +169,86 @@ __device__ __forceinline__ float sum_bf16x8(bf16x8_t v, float acc) {
 // Q fragment of one query row as the B operand of S^T = K Q^T: element
 // (ks, e) is column ks * 16 + g * 8 + e.  The row is optionally rotated by
 // the 3D RoPE (rounded to bf16, exactly as vx_rope3d_apply stores it), then
-// multiplied by scale * log2(e) and rounded to bf16.
+// multiplied by scale * log2(e) and rounded to bf16.  The lane holds
+// columns g * 8 .. g * 8 + 7 of every 16: with adjacent pairs, or with the
+// head split in halves (column c pairs with c + D/2, which is k-step
+// ks + D/32, same e), both elements of each pair are in the lane; with
+// band halves the partner is read from memory.
 template <int D>
 __device__ __forceinline__ void load_q_fragment(const FaArgs& a, const uint16_t* qb, int64_t qi,
                                                 int g, bf16x8_t* qf) {
+    constexpr int NKS = D / 16;
+    uint32_t u[NKS][4];
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
+    for (int ks = 0; ks < NKS; ++ks) {
         uint4 w = {0u, 0u, 0u, 0u};
         if (qi < a.nq) w = *(const uint4*)(qb + qi * a.row_stride + ks * 16 + g * 8);
-        uint32_t u[4] = {w.x, w.y, w.z, w.w};
-        if (a.use_rope && qi < a.nq && a.rope.pairing == 0) {
+        u[ks][0] = w.x; u[ks][1] = w.y; u[ks][2] = w.z; u[ks][3] = w.w;
+    }
+    int tp = 0, hp = 0, wp = 0;
+    const bool rot = a.use_rope && qi < a.nq && rope_token_pos(a.rope, qi, &tp, &hp, &wp);
+    if (rot && a.rope.pairing == 0) {
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
                 const int pair = (ks * 16 + g * 8) / 2 + m;
-                int pos, j, width;
-                if (rope_pair_geometry(a.rope, qi, pair, &pos, &j, &width)) {
-                    float c, s;
-                    rope_cos_sin(a.rope, pos, j, width, &c, &s);
-                    float x0 = bf16_lo(u[m]), x1 = bf16_hi(u[m]);
-                    rope_rotate(x0, x1, c, s);
-                    u[m] = pack_bf16x2(x0, x1);
-                }
+                float c, s;
+                rope_cos_sin(a.rope, rope_pair_pos(a.rope, pair, tp, hp, wp), pair, &c, &s);
+                float x0 = bf16_lo(u[ks][m]), x1 = bf16_hi(u[ks][m]);
+                rope_rotate(x0, x1, c, s);
+                u[ks][m] = pack_bf16x2(x0, x1);
             }
-        } else if (a.use_rope && qi < a.nq) {
-            // half-split pairings: the partner element lies elsewhere in the
-            // row and is read from memory (once per workgroup, before the
-            // key loop)
-            const uint16_t* qrow = qb + qi * a.row_stride;
+    } else if (rot && a.rope.pairing == 1) {
+#pragma unroll
+        for (int ks = 0; ks < NKS / 2; ++ks) {
+            float f0[8], f1[8];
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                f0[2 * m] = bf16_lo(u[ks][m]);
+                f0[2 * m + 1] = bf16_hi(u[ks][m]);
+                f1[2 * m] = bf16_lo(u[ks + NKS / 2][m]);
+                f1[2 * m + 1] = bf16_hi(u[ks + NKS / 2][m]);
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int pair = ks * 16 + g * 8 + e;
+                float c, s;
+                rope_cos_sin(a.rope, rope_pair_pos(a.rope, pair, tp, hp, wp), pair, &c, &s);
+                rope_rotate(f0[e], f1[e], c, s);
+            }
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                u[ks][m] = pack_bf16x2(f0[2 * m], f0[2 * m + 1]);
+                u[ks + NKS / 2][m] = pack_bf16x2(f1[2 * m], f1[2 * m + 1]);
+            }
+        }
+    } else if (rot) {
+        const uint16_t* qrow = qb + qi * a.row_stride;
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
             float out[8];
 #pragma unroll
-            for (int m = 0; m < 8; ++m) {
-                const int e = ks * 16 + g * 8 + m;
-                const float xe = (m & 1) ? bf16_hi(u[m >> 1]) : bf16_lo(u[m >> 1]);
-                int pair, partner, pos, j, width;
+            for (int e = 0; e < 8; ++e) {
+                const float xe = (e & 1) ? bf16_hi(u[ks][e >> 1]) : bf16_lo(u[ks][e >> 1]);
+                int pair, partner;
                 bool second;
-                rope_elem_pair(a.rope, e, &pair, &partner, &second);
-                out[m] = xe;
-                if (rope_pair_geometry(a.rope, qi, pair, &pos, &j, &width)) {
-                    float c, s;
-                    rope_cos_sin(a.rope, pos, j, width, &c, &s);
-                    const float xp = __uint_as_float((uint32_t)qrow[partner] << 16);
-                    out[m] = rope_rotate_elem(xe, xp, second, c, s);
-                }
+                rope_elem_pair(a.rope, ks * 16 + g * 8 + e, &pair, &partner, &second);
+                float c, s;
+                rope_cos_sin(a.rope, rope_pair_pos(a.rope, pair, tp, hp, wp), pair, &c, &s);
+                const float xp = __uint_as_float((uint32_t)qrow[partner] << 16);
+                out[e] = rope_rotate_elem(xe, xp, second, c, s);
             }
 #pragma unroll
-            for (int m = 0; m < 4; ++m) u[m] = pack_bf16x2(out[2 * m], out[2 * m + 1]);
+            for (int m = 0; m < 4; ++m) u[ks][m] = pack_bf16x2(out[2 * m], out[2 * m + 1]);
         }
+    }
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
 #pragma unroll
         for (int m = 0; m < 4; ++m)
-            u[m] = pack_bf16x2(bf16_lo(u[m]) * a.scale_log2, bf16_hi(u[m]) * a.scale_log2);
-        qf[ks] = __builtin_bit_cast(bf16x8_t, uint4{u[0], u[1], u[2], u[3]});
+            u[ks][m] = pack_bf16x2(bf16_lo(u[ks][m]) * a.scale_log2, bf16_hi(u[ks][m]) * a.scale_log2);
+        qf[ks] = __builtin_bit_cast(bf16x8_t, uint4{u[ks][0], u[ks][1], u[ks][2], u[ks][3]});
     }
 }
 
@@ -909,31 +939,28 @@ void fa_fwd_f32_kernel(FaArgs a) {
         qv[e] = qi < nq ? qb[qi * a.row_stride + part * 32 + e] : 0.f;
         acc[e] = 0.f;
     }
-    if (a.use_rope && qi < nq && a.rope.pairing == 0) {
+    int tp = 0, hp = 0, wp = 0;
+    const bool rot = a.use_rope && qi < nq && rope_token_pos(a.rope, qi, &tp, &hp, &wp);
+    if (rot && a.rope.pairing == 0) {
 #pragma unroll
         for (int m = 0; m < 16; ++m) {
-            int pos, j, width;
-            if (rope_pair_geometry(a.rope, qi, part * 16 + m, &pos, &j, &width)) {
-                float c, s;
-                rope_cos_sin(a.rope, pos, j, width, &c, &s);
-                rope_rotate(qv[2 * m], qv[2 * m + 1], c, s);
-            }
+            const int pair = part * 16 + m;
+            float c, s;
+            rope_cos_sin(a.rope, rope_pair_pos(a.rope, pair, tp, hp, wp), pair, &c, &s);
+            rope_rotate(qv[2 * m], qv[2 * m + 1], c, s);
         }
-    } else if (a.use_rope && qi < nq) {
+    } else if (rot) {
         // half-split pairings: partners are read from the row in memory
         const float* qrow = qb + qi * a.row_stride;
         float out[32];
 #pragma unroll
         for (int e = 0; e < 32; ++e) {
-            int pair, partner, pos, j, width;
+            int pair, partner;
             bool second;
             rope_elem_pair(a.rope, part * 32 + e, &pair, &partner, &second);
-            out[e] = qv[e];
-            if (rope_pair_geometry(a.rope, qi, pair, &pos, &j, &width)) {
-                float c, s;
-                rope_cos_sin(a.rope, pos, j, width, &c, &s);
-                out[e] = rope_rotate_elem(qv[e], qrow[partner], second, c, s);
-            }
+            float c, s;
+            rope_cos_sin(a.rope, rope_pair_pos(a.rope, pair, tp, hp, wp), pair, &c, &s);
+            out[e] = rope_rotate_elem(qv[e], qrow[partner], second, c, s);
         }
 #pragma unroll
         for (int e = 0; e < 32; ++e) qv[e] = out[e];
@@ -1011,7 +1038,7 @@ hipError_t launch_flash_attn(const void* q, const void* k, const void* v, void* 
     a.scale_log2 = scale * 1.4426950408889634f;
     a.use_rope = rope != nullptr;
     if (rope) a.rope = *rope;
-    else a.rope = RopeArgs{1, 1, 1, 0, 0, 0, 0, 1.f, 0};
+    else a.rope = RopeArgs{};
 
     const int rows_per_wg = flash_attn_rows_per_workgroup(bf16, head_dim);
     a.n_qtiles = (int)((nq + rows_per_wg - 1) / rows_per_wg);

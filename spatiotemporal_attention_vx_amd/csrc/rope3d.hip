@@ -21,7 +21,7 @@
 namespace vx {
 
 constexpr int ROPE_TPB = 4;          // tokens per workgroup
-constexpr int ROPE_MAX_HALF = 128;   // head_dim <= 256
+constexpr int ROPE_MAX_HALF = ROPE_MAX_PAIRS;
 
 template <bool BF16>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256)))
@@ -36,9 +36,9 @@ void rope3d_kernel(uint4* q, uint4* k, int64_t rows, int64_t n_tokens, int heads
         const int tk = i / half, pair = i - tk * half;
         const int64_t row = row0 + tk;
         float c = 1.f, s = 0.f;
-        int pos, j, width;
-        if (row < rows && rope_pair_geometry(r, row % n_tokens, pair, &pos, &j, &width))
-            rope_cos_sin(r, pos, j, width, &c, &s);
+        int tp, hp, wp;
+        if (row < rows && rope_token_pos(r, row % n_tokens, &tp, &hp, &wp))
+            rope_cos_sin(r, rope_pair_pos(r, pair, tp, hp, wp), pair, &c, &s);
         cs[i] = f32x2_t{c, s};
     }
     __shared__ int rotate[ROPE_TPB];     // token exists and is not text
@@ -88,19 +88,31 @@ void rope3d_kernel(uint4* q, uint4* k, int64_t rows, int64_t n_tokens, int heads
     }
 }
 
-// Half-split pairings.  The (token, tensor, head) rows of the workgroup's
-// tokens are taken 256 / (head_dim / EPC) at a time: one thread per 16-byte
-// chunk loads it, keeps its values and writes them to LDS; after a barrier
-// each thread rotates its elements with their partners from LDS and stores
-// its chunk back.
+// Half-split pairings.  Each wave works through its own share of the
+// workgroup's (token, tensor, head) rows, 64 / (head_dim / EPC) rows per
+// pass and ROPE_SPLIT_U passes at once: every lane loads one 16-byte chunk
+// of each of its U rows (U loads in flight), keeps the values and writes
+// them to the wave's own LDS area; the wave then rotates every element with
+// its partner read from LDS and stores the chunks back.  Only lanes of one
+// wave share an LDS area, so a wave-level barrier orders the writes and the
+// reads; waves never wait for each other inside the loop.
+constexpr int ROPE_SPLIT_U = 2;
+
+__device__ __forceinline__ void wave_sync_lds() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 template <bool BF16>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256)))
 void rope3d_split_kernel(uint4* q, uint4* k, int64_t rows, int64_t n_tokens, int heads,
                          int head_dim, RopeArgs r) {
     constexpr int EPC = BF16 ? 8 : 4;
+    constexpr int U = ROPE_SPLIT_U;
     __shared__ f32x2_t cs[ROPE_TPB * ROPE_MAX_HALF];
-    __shared__ float xs[256 * EPC];      // staged head rows
-    __shared__ int rotate[ROPE_TPB];     // token exists and is not text
+    __shared__ float xs[4][U * 64 * EPC];   // per wave: U passes x 64 lanes x EPC values
+    __shared__ int rotate[ROPE_TPB];        // token exists and is not text
     const int half = head_dim >> 1;
     const int64_t row0 = (int64_t)blockIdx.x * ROPE_TPB;
 
@@ -108,9 +120,9 @@ void rope3d_split_kernel(uint4* q, uint4* k, int64_t rows, int64_t n_tokens, int
         const int tk = i / half, pair = i - tk * half;
         const int64_t row = row0 + tk;
         float c = 1.f, s = 0.f;
-        int pos, j, width;
-        if (row < rows && rope_pair_geometry(r, row % n_tokens, pair, &pos, &j, &width))
-            rope_cos_sin(r, pos, j, width, &c, &s);
+        int tp, hp, wp;
+        if (row < rows && rope_token_pos(r, row % n_tokens, &tp, &hp, &wp))
+            rope_cos_sin(r, rope_pair_pos(r, pair, tp, hp, wp), pair, &c, &s);
         cs[i] = f32x2_t{c, s};
     }
     if (threadIdx.x < ROPE_TPB) {
@@ -119,41 +131,63 @@ void rope3d_split_kernel(uint4* q, uint4* k, int64_t rows, int64_t n_tokens, int
     }
     __syncthreads();
 
-    const int dpr = head_dim / EPC;              // chunks per head row
-    const int per_iter = 256 / dpr;              // head rows per pass
-    const int slot = threadIdx.x / dpr, c = threadIdx.x - slot * dpr;
-    const int64_t units = (int64_t)ROPE_TPB * 2 * heads;   // (token, tensor, head), head fastest
-    float* const mine = xs + slot * head_dim;
-    for (int64_t u0 = 0; u0 < units; u0 += per_iter) {
-        const int64_t u = u0 + slot;
-        bool live = slot < per_iter && u < units;
-        const int h = live ? (int)(u % heads) : 0, tw = live ? (int)(u / heads) : 0;
-        const int which = tw & 1, tk = tw >> 1;
-        uint4* base = which ? k : q;
-        live = live && base != nullptr && rotate[tk];
-        uint4* p = live ? base + ((row0 + tk) * heads + h) * dpr + c : nullptr;
-        float f[EPC];
-        if (live) {
-            const uint4 v = *p;
-            unpack_chunk<BF16>(u32x4_t{v.x, v.y, v.z, v.w}, f);
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int dpr = head_dim / EPC;            // chunks per head row (<= 32)
+    const int rpp = 64 / dpr;                  // head rows per pass
+    const int slot = lane / dpr, c = lane - slot * dpr;
+    // a lane always holds the same columns: their pairs are fixed
+    int pair[EPC], partner[EPC];
+    uint32_t second = 0;
 #pragma unroll
-            for (int m = 0; m < EPC; ++m) mine[c * EPC + m] = f[m];
+    for (int m = 0; m < EPC; ++m) {
+        bool sec;
+        rope_elem_pair(r, c * EPC + m, &pair[m], &partner[m], &sec);
+        second |= (uint32_t)sec << m;
+    }
+    const int64_t units = (int64_t)ROPE_TPB * 2 * heads;   // (token, tensor, head), head fastest
+    float* const area = xs[wave];
+    // passes p = 0, 1, ... cover units p * rpp .. p * rpp + rpp - 1; wave w
+    // takes passes w * U .. w * U + U - 1, then 4 U further on, and so on
+    for (int64_t p0 = wave * U; p0 * rpp < units; p0 += 4 * U) {
+        float f[U][EPC];
+        uint4* ptr[U];
+        int tku[U];
+#pragma unroll
+        for (int i = 0; i < U; ++i) {
+            const int64_t u = (p0 + i) * rpp + slot;
+            bool live = slot < rpp && u < units;
+            const int h = live ? (int)(u % heads) : 0, tw = live ? (int)(u / heads) : 0;
+            const int which = tw & 1, tk = tw >> 1;
+            uint4* base = which ? k : q;
+            live = live && base != nullptr && rotate[tk];
+            tku[i] = tk;
+            ptr[i] = live ? base + ((row0 + tk) * heads + h) * dpr + c : nullptr;
+            if (live) {
+                const uint4 v = *ptr[i];
+                unpack_chunk<BF16>(u32x4_t{v.x, v.y, v.z, v.w}, f[i]);
+            }
         }
-        __syncthreads();
-        if (live) {
+#pragma unroll
+        for (int i = 0; i < U; ++i)
+            if (ptr[i] != nullptr)
+#pragma unroll
+                for (int m = 0; m < EPC; ++m) area[(i * rpp + slot) * head_dim + c * EPC + m] = f[i][m];
+        wave_sync_lds();
+#pragma unroll
+        for (int i = 0; i < U; ++i) {
+            if (ptr[i] == nullptr) continue;
+            const float* row = area + (i * rpp + slot) * head_dim;
+            const f32x2_t* cst = cs + tku[i] * half;
             float out[EPC];
 #pragma unroll
             for (int m = 0; m < EPC; ++m) {
-                int pair, partner;
-                bool second;
-                rope_elem_pair(r, c * EPC + m, &pair, &partner, &second);
-                const f32x2_t e = cs[tk * half + pair];
-                out[m] = rope_rotate_elem(f[m], mine[partner], second, e.x, e.y);
+                const f32x2_t e = cst[pair[m]];
+                out[m] = rope_rotate_elem(f[i][m], row[partner[m]], (second >> m) & 1, e.x, e.y);
             }
             const u32x4_t w = pack_chunk<BF16>(out);
-            *p = uint4{w[0], w[1], w[2], w[3]};
+            *ptr[i] = uint4{w[0], w[1], w[2], w[3]};
         }
-        __syncthreads();
+        wave_sync_lds();   // this pass's reads are done before the next pass writes
     }
 }
 

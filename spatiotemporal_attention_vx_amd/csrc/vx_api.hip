@@ -96,8 +96,18 @@ int check_rope(const char* fn, const vx_rope3d_desc* r, int64_t n_tokens, int64_
     if (r->pairing < 0 || r->pairing > 2)
         return fail(VX_ERR_INVALID, "%s: rope pairing %d is not 0 (adjacent), 1 (head halves) "
                     "or 2 (band halves)", fn, r->pairing);
-    *out = vx::RopeArgs{r->T, r->H, r->W, r->n_prefix, r->d_t, r->d_h, r->d_w, r->theta,
-                        r->pairing};
+    if (head_dim / 2 > vx::ROPE_MAX_PAIRS)
+        return fail(VX_ERR_UNSUPPORTED, "%s: rope head_dim %lld above %d", fn, (long long)head_dim,
+                    2 * vx::ROPE_MAX_PAIRS);
+    vx::RopeArgs a{};
+    a.T = r->T; a.H = r->H; a.W = r->W; a.n_prefix = r->n_prefix;
+    a.d_t = r->d_t; a.d_h = r->d_h; a.d_w = r->d_w; a.pairing = r->pairing;
+    // pair j of band a turns at theta^(-2j / d_a); bands listed t, h, w
+    int pair = 0;
+    for (int width : {r->d_t, r->d_h, r->d_w})
+        for (int j = 0; j < width / 2; ++j)
+            a.freq[pair++] = std::pow((double)r->theta, -2.0 * j / (double)width);
+    *out = a;
     return VX_OK;
 }
 

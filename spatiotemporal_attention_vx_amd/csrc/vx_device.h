@@ -52,34 +52,39 @@ __device__ __forceinline__ u32x4_t pack_chunk(const float* f) {
 }
 
 // RoPE geometry of one call, in kernel-argument form.
+constexpr int ROPE_MAX_PAIRS = 128;   // head_dim <= 256
 struct RopeArgs {
     int32_t T, H, W;
     int32_t n_prefix;
     int32_t d_t, d_h, d_w;
-    float theta;
     int32_t pairing;   // 0 adjacent pairs, 1 halves of the head, 2 halves of each band
+    // theta^(-2j / d_a) of every pair in angle order ([t | h | w] bands),
+    // evaluated once per call on the host in double precision
+    double freq[ROPE_MAX_PAIRS];
 };
 
-// Position along the band that pair `pair` of the head dimension belongs
-// to, and that pair's index and width inside its band.  Returns false for
-// text-prefix tokens (no rotation).
-__device__ __forceinline__ bool rope_pair_geometry(const RopeArgs& r, int64_t token, int pair,
-                                                    int* pos, int* j, int* width) {
+// Grid position (t, h, w) of a token; false for text-prefix tokens (no
+// rotation).  Evaluated once per token row, never per pair.
+__device__ __forceinline__ bool rope_token_pos(const RopeArgs& r, int64_t token, int* t, int* h,
+                                               int* w) {
     if (token < r.n_prefix) return false;
     const int64_t v = token - r.n_prefix;
     const int64_t hw = (int64_t)r.H * r.W;
-    const int t = (int)(v / hw);
-    const int h = (int)((v / r.W) % r.H);
-    const int w = (int)(v % r.W);
-    const int pt = r.d_t >> 1, ph = r.d_h >> 1;
-    if (pair < pt) { *pos = t; *j = pair; *width = r.d_t; }
-    else if (pair < pt + ph) { *pos = h; *j = pair - pt; *width = r.d_h; }
-    else { *pos = w; *j = pair - pt - ph; *width = r.d_w; }
+    *t = (int)(v / hw);
+    const int rem = (int)(v - (int64_t)(*t) * hw);    // < H * W
+    *h = rem / r.W;
+    *w = rem - *h * r.W;
     return true;
 }
 
+// Position along the band that pair `pair` (angle order) belongs to.
+__device__ __forceinline__ int rope_pair_pos(const RopeArgs& r, int pair, int t, int h, int w) {
+    const int pt = r.d_t >> 1, ph = r.d_h >> 1;
+    return pair < pt ? t : (pair < pt + ph ? h : w);
+}
+
 // Pair of element e of the head dimension under the call's pairing: the
-// pair's index in angle order ([t | h | w] bands, as rope_pair_geometry
+// pair's index in angle order ([t | h | w] bands, as rope_pair_pos
 // numbers them), the other element of the pair, and whether e is the
 // pair's second element (the imaginary part of a + i b).
 __device__ __forceinline__ void rope_elem_pair(const RopeArgs& r, int e, int* pair, int* partner,
@@ -111,16 +116,32 @@ __device__ __forceinline__ float rope_rotate_elem(float xe, float xp, bool secon
     return second ? __builtin_fmaf(xp, s, xe * c) : __builtin_fmaf(xe, c, -xp * s);
 }
 
-// cos and sin of the RoPE angle pos * theta^(-2j/width), evaluated in double
-// precision and rounded to float once.  Called once per (token, pair), never
-// per head, so its cost is spread over all heads and over Q and K.
-__device__ __forceinline__ void rope_cos_sin(const RopeArgs& r, int pos, int j, int width,
-                                             float* c, float* s) {
-    const double freq = exp2(-(2.0 * j / (double)width) * log2((double)r.theta));
-    double sd, cd;
-    sincos((double)pos * freq, &sd, &cd);
-    *c = (float)cd;
-    *s = (float)sd;
+// cos and sin of pair `pair`'s RoPE angle at grid position pos.  The angle
+// pos * freq is formed in double precision and reduced by multiples of
+// pi/2 there (exact to ~1e-15 rad for any grid index); sin and cos of the
+// remainder r (|r| <= pi/4) come from their Taylor series in float, to r^9
+// and r^10 (truncation below 2e-9), and the quadrant picks signs and order.
+// Branch-free; absolute error a few 1e-7.
+__device__ __forceinline__ void rope_cos_sin(const RopeArgs& r, int pos, int pair, float* c,
+                                             float* s) {
+    const double ang = (double)pos * r.freq[pair];
+    const double qd = __builtin_rint(ang * 0.63661977236758134308);        // 2 / pi
+    double red = __builtin_fma(-qd, 1.57079632679489655800, ang);          // pi/2, high part
+    red = __builtin_fma(-qd, 6.12323399573676588613e-17, red);             // pi/2, low part
+    const float x = (float)red, x2 = x * x;
+    float sn = __builtin_fmaf(x2, 1.0f / 362880.0f, -1.0f / 5040.0f);
+    sn = __builtin_fmaf(x2, sn, 1.0f / 120.0f);
+    sn = __builtin_fmaf(x2, sn, -1.0f / 6.0f);
+    sn = __builtin_fmaf(x2 * x, sn, x);
+    float cn = __builtin_fmaf(x2, -1.0f / 3628800.0f, 1.0f / 40320.0f);
+    cn = __builtin_fmaf(x2, cn, -1.0f / 720.0f);
+    cn = __builtin_fmaf(x2, cn, 1.0f / 24.0f);
+    cn = __builtin_fmaf(x2, cn, -0.5f);
+    cn = __builtin_fmaf(x2, cn, 1.0f);
+    const int quad = (int)((int64_t)qd & 3);
+    const float s_ = (quad & 1) ? cn : sn, c_ = (quad & 1) ? sn : cn;
+    *s = (quad & 2) ? -s_ : s_;
+    *c = ((quad + 1) & 2) ? -c_ : c_;
 }
 
 // Rotate the pair (x0, x1) by (c, s).
