@@ -10,6 +10,7 @@
  * and, for attention whose keys are split into parts (sharded or in
  * passes):
  *   vx_flash_attn_fwd_kv  attention of one token set over another
+ *   vx_flash_attn_fwd_masked  the same with a padded key range per sample
  *   vx_attn_merge2        two partial results combined through their LSEs
  *
  * Conventions shared by every entry point
@@ -185,6 +186,29 @@ int vx_flash_attn_fwd_kv(const void* q, const void* k, const void* v, void* o, f
                          int64_t batch, int64_t n_q, int64_t n_kv, int64_t heads,
                          int64_t head_dim, float softmax_scale, const vx_rope3d_desc* rope_q,
                          int dt, void* hip_stream);
+
+/*
+ * Attention with key padding: as vx_flash_attn_fwd_kv, with keys
+ * key_pad[2 b] <= j < key_pad[2 b + 1] of batch entry b taking no weight
+ * (excluded from the softmax sum).  The vidax pages run CogVideoX's joint
+ * text+video attention over a fixed-length text prefix (paper §3.1
+ * "CogVideoX"), and report that padding left unmasked drifts CogVideoX's
+ * T5 text embeddings in bf16 (agihunt.info summary); a padded range of keys
+ * is what such a mask removes: the padded tail of a text prefix, or
+ * [len_b, n_kv) for a padded key tail.
+ *
+ * key_pad: HOST array of 2 * batch int32 (lo, hi) pairs, read during the
+ * call (not kept); lo == hi masks nothing for that entry.  batch <= 64.
+ * Other arguments as vx_flash_attn_fwd_kv; lse of a row is the log-sum-exp
+ * over its unmasked keys.
+ * Errors: as vx_flash_attn_fwd_kv; VX_ERR_NULL (key_pad NULL);
+ * VX_ERR_INVALID (a range outside 0 <= lo <= hi <= n_kv, or one that
+ * leaves no valid key); VX_ERR_UNSUPPORTED (batch > 64).
+ */
+int vx_flash_attn_fwd_masked(const void* q, const void* k, const void* v, void* o, float* lse,
+                             int64_t batch, int64_t n_q, int64_t n_kv, int64_t heads,
+                             int64_t head_dim, float softmax_scale, const vx_rope3d_desc* rope_q,
+                             const int32_t* key_pad, int dt, void* hip_stream);
 
 /*
  * Merge of two partial attention results over disjoint key sets A and B

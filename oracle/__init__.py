@@ -13,6 +13,7 @@ Each function writes out the plain definition of what the step computes:
 * ``rope3d.rope3d_apply``    3D RoPE as complex multiplication per band
 * ``attention.attention``    naive softmax(Q K^T * scale) V, whole score row
 * ``attention.attention_rope`` RoPE on Q and K, then attention
+* ``attention.attention_masked``  attention with a padded key range left out
 * ``attention.merge_lse``    two partial attentions over disjoint key sets,
   combined through their log-sum-exps
 
@@ -31,9 +32,10 @@ convention is parity unpinned; the invariants pin everything else.
 """
 from .adaln import adaln_modulate, adaln_modulate_per_sample, layer_norm
 from .rope3d import token_positions, rope_angles, rope3d_apply
-from .attention import attention, attention_rope, merge_lse, softmax_rows
+from .attention import attention, attention_masked, attention_rope, merge_lse, softmax_rows
 
 __all__ = [
     "adaln_modulate", "adaln_modulate_per_sample", "layer_norm", "token_positions", "rope_angles",
-    "rope3d_apply", "attention", "attention_rope", "merge_lse", "softmax_rows",
+    "rope3d_apply", "attention", "attention_masked", "attention_rope", "merge_lse",
+    "softmax_rows",
 ]

@@ -17,6 +17,9 @@ No mask, no causality, no dropout.  scale defaults to 1 / sqrt(head_dim).
 The queries and the keys may be different token sets (q has its own row
 count), which is attention over one part of a key-split sequence.
 
+``attention_masked`` leaves a range of keys out of the softmax (key
+padding, e.g. the padded tail of a joint sequence's text prefix).
+
 ``merge_lse`` combines two such partial results over disjoint key sets.
 From the definition, exp(lse) is a row's softmax denominator Z and o its
 Z-weighted mean of values, so over the union
@@ -64,6 +67,20 @@ def attention(q, k, v, scale: float = 0.0, rows=None, row_block: int = 512):
             o[r0:r0 + sel.size, h, :] = (e @ vh) / total
             lse[h, r0:r0 + sel.size] = m[:, 0] + np.log(total[:, 0])
     return o, lse
+
+
+def attention_masked(q, k, v, lo: int, hi: int, scale: float = 0.0, rows=None):
+    """Attention in which keys lo <= j < hi take no weight (key padding).
+
+    The plain definition: the softmax runs over the remaining keys only,
+    so this is ``attention`` over K and V with those rows removed.  At
+    least one key must remain.  Returns (o [R, H, d], lse [H, R]).
+    """
+    keep = np.ones(k.shape[0], dtype=bool)
+    keep[lo:hi] = False
+    if not keep.any():
+        raise ValueError("every key is masked")
+    return attention(q, k[keep], v[keep], scale, rows)
 
 
 def merge_lse(o_a, lse_a, o_b, lse_b):

@@ -16,8 +16,9 @@ from . import build as _build
 VX_F32, VX_BF16 = 0, 1
 STATUS = {0: "VX_OK", 1: "VX_ERR_NULL", 2: "VX_ERR_INVALID", 3: "VX_ERR_UNSUPPORTED",
           4: "VX_ERR_ALIGN", 5: "VX_ERR_HIP"}
-EXPORTS = ("vx_adaln_modulate", "vx_adaln_modulate_ex", "vx_rope3d_apply", "vx_flash_attn_fwd", "vx_flash_attn_fwd_kv",
-           "vx_attn_merge2", "vx_last_error", "vx_version")
+EXPORTS = ("vx_adaln_modulate", "vx_adaln_modulate_ex", "vx_rope3d_apply", "vx_flash_attn_fwd",
+           "vx_flash_attn_fwd_kv", "vx_flash_attn_fwd_masked", "vx_attn_merge2", "vx_last_error",
+           "vx_version")
 
 
 class VxError(RuntimeError):
@@ -65,6 +66,10 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.vx_flash_attn_fwd_kv.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
                                          ctypes.c_float, ctypes.POINTER(RopeDesc), ctypes.c_int, vp]
     lib.vx_flash_attn_fwd_kv.restype = ctypes.c_int
+    lib.vx_flash_attn_fwd_masked.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
+                                             ctypes.c_float, ctypes.POINTER(RopeDesc), vp,
+                                             ctypes.c_int, vp]
+    lib.vx_flash_attn_fwd_masked.restype = ctypes.c_int
     lib.vx_attn_merge2.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_int, vp]
     lib.vx_attn_merge2.restype = ctypes.c_int
     lib.vx_last_error.argtypes = []
@@ -199,6 +204,27 @@ def flash_attn_fwd_kv(q, k, v, o, lse=None, softmax_scale: float = 0.0,
                                        h, d, softmax_scale,
                                        ctypes.byref(rope_q) if rope_q is not None else None,
                                        _dtype_code(q), _stream(stream)))
+    return o
+
+
+def flash_attn_fwd_masked(q, k, v, o, key_pad, lse=None, softmax_scale: float = 0.0,
+                          rope_q: RopeDesc | None = None, stream=None):
+    """As flash_attn_fwd_kv; keys lo <= j < hi of sample b (key_pad[b] = (lo, hi)) take no weight."""
+    _same(q, o, names=("q", "o"))
+    _same(k, v, names=("k", "v"))
+    b, nq, h, d = q.shape
+    if k.dtype != q.dtype or k.shape[0] != b or tuple(k.shape[2:]) != (h, d):
+        raise ValueError(f"k is {tuple(k.shape)} {k.dtype}, q is {tuple(q.shape)} {q.dtype}")
+    pads = [(int(lo), int(hi)) for lo, hi in key_pad]
+    if len(pads) != b:
+        raise ValueError(f"key_pad has {len(pads)} entries, batch is {b}")
+    arr = (ctypes.c_int32 * (2 * b))(*[x for p in pads for x in p])
+    _check_lse(lse, b, h, nq)
+    _check(load().vx_flash_attn_fwd_masked(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), b, nq,
+                                           k.shape[1], h, d, softmax_scale,
+                                           ctypes.byref(rope_q) if rope_q is not None else None,
+                                           ctypes.cast(arr, ctypes.c_void_p), _dtype_code(q),
+                                           _stream(stream)))
     return o
 
 

@@ -45,6 +45,11 @@
 //   * Tiles past the sequence end are read through a buffer resource that
 //     ends at the sequence end, so they load as zeros with no per-lane test;
 //     scores of keys past the end are set to -inf in the last real tile.
+//   * Key padding (a per-batch key range that takes no weight, e.g. the
+//     padded tail of a joint sequence's text prefix): the tiles that hold
+//     padded keys get -inf there, in the same rare branch as the last tile;
+//     the key loop starts at a tile with a valid key (FaTiles), so the
+//     running maximum is finite from the first tile on.
 //   * Workgroups are remapped so each XCD works through a contiguous range
 //     of (batch, head, query tile), keeping that head's K/V hot in its L2.
 //
@@ -64,6 +69,8 @@
 
 namespace vx {
 
+constexpr int FA_MAX_PAD_BATCH = 64;   // batch entries a key-padding call may have
+
 struct FaArgs {
     const uint16_t* q;
     const uint16_t* k;
@@ -82,11 +89,52 @@ struct FaArgs {
     float scale_log2;      // scale * log2(e)
     int use_rope;
     RopeArgs rope;
+    // Key padding: keys pad_lo[b] <= j < pad_hi[b] of batch entry b take no
+    // weight (lo == hi: none); at least one key of every entry is valid.
+    int has_pad;
+    int32_t pad_lo[FA_MAX_PAD_BATCH], pad_hi[FA_MAX_PAD_BATCH];
 };
 
 // ---------------------------------------------------------------- bf16 MFMA
 
 constexpr int FA_BC = 64;    // keys per tile
+
+// Key-tile order of one (batch, head).  Without key padding (PAD false)
+// tiles run 0 .. nt - 1 and only the last can hold dead keys (past the
+// end).  With padding, tiles run t0, t0 + 1, .., nt - 1, 0, .., t0 - 1: t0
+// is 0 unless the padded range starts at key 0, in which case it is the
+// tile holding key pad_hi, so the first tile always has a valid key and the
+// running maximum starts finite.  Step indices at or past nt (prefetches
+// beyond the last step) map to themselves and load as zeros.
+template <bool PAD>
+struct FaTiles {
+    int nt, t0;
+    int64_t nk, lo, hi;
+    bool tail;
+    __device__ FaTiles(const FaArgs& a, int64_t b) {
+        nk = a.nk;
+        nt = (int)((nk + FA_BC - 1) / FA_BC);
+        lo = PAD ? a.pad_lo[b] : 0;
+        hi = PAD ? a.pad_hi[b] : 0;
+        t0 = (PAD && lo == 0 && hi > 0) ? (int)(hi / FA_BC) : 0;
+        tail = (nk % FA_BC) != 0;
+    }
+    __device__ int at(int i) const {
+        if constexpr (!PAD) return i;
+        const int t = i + t0;
+        return i >= nt ? i : (t >= nt ? t - nt : t);
+    }
+    // does tile tt hold a key past the end or a padded key
+    __device__ bool masked(int tt) const {
+        if constexpr (!PAD) return tail && tt == nt - 1;
+        const int64_t kv0 = (int64_t)tt * FA_BC;
+        return (tail && tt == nt - 1) || (kv0 < hi && kv0 + FA_BC > lo);
+    }
+    __device__ bool dead(int64_t key) const {
+        if constexpr (!PAD) return key >= nk;
+        return (key >= nk) | ((key >= lo) & (key < hi));
+    }
+};
 constexpr int FA_PAD = 8;    // LDS row padding of K and V^T (elements)
 constexpr int FA_WAVES = VX_FA_WAVES;   // waves per workgroup
 constexpr int FA_QG = VX_FA_QG;         // 32-row query groups per wave
@@ -252,7 +300,7 @@ __device__ __forceinline__ void load_q_fragment(const FaArgs& a, const uint16_t*
     }
 }
 
-template <int D, int WAVES, int QG>
+template <int D, int WAVES, int QG, bool PAD>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * WAVES, 64 * WAVES),
                           amdgpu_waves_per_eu(3 - QG, 3 - QG)))
 void fa_fwd_bf16_kernel(FaArgs a) {
@@ -276,7 +324,8 @@ void fa_fwd_bf16_kernel(FaArgs a) {
     const uint16_t* kb = a.k + kv_off;
     const uint16_t* vb = a.v + kv_off;
     const int64_t nq = a.nq, nk = a.nk;
-    const int nt = (int)((nk + FA_BC - 1) / FA_BC);
+    const FaTiles<PAD> tl(a, b);
+    const int nt = tl.nt;
 
     // query group qg of this wave: rows (wave * QG + qg) * 32 + l32 of the tile
     int64_t qi[QG];
@@ -365,7 +414,7 @@ void fa_fwd_bf16_kernel(FaArgs a) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 const int64_t key = kv0 + kb2 * 32 + 8 * (i >> 2) + 4 * g + (i & 3);
-                if (key >= nk) s[kb2][i] = -__builtin_inff();
+                if (tl.dead(key)) s[kb2][i] = -__builtin_inff();
             }
     };
     auto row_max = [&](const f32x16_t* s) {
@@ -388,27 +437,26 @@ void fa_fwd_bf16_kernel(FaArgs a) {
         l_run[qg] = 0.f;
         mx_next[qg] = 0.f;
     }
-    const bool tail = (nk % FA_BC) != 0;
-
     // ---- prologue: K(0), K(1), K(2) and V(0) into LDS; S(0); m from tile 0
+    // (step indices; tl.at maps them to key tiles)
     f32x16_t sA[QG][2], sB[QG][2];
-    load_k(0);
-    load_v(0);
+    load_k(tl.at(0));
+    load_v(tl.at(0));
     store_k(kbuf[0]);
     store_v(vbuf[0]);
-    load_k(1);
+    load_k(tl.at(1));
     store_k(kbuf[1]);
-    load_k(2);
+    load_k(tl.at(2));
     store_k(kbuf[2]);
     __syncthreads();
 #pragma unroll
     for (int qg = 0; qg < QG; ++qg) scores(sA[qg], kbuf[0], qf[qg], negm[qg]);
     __syncthreads();              // kbuf[0] is refilled in the first iteration
-    load_k(3);
-    load_v(1);
+    load_k(tl.at(3));
+    load_v(tl.at(1));
 #pragma unroll
     for (int qg = 0; qg < QG; ++qg) {
-        if (nt == 1 && tail) mask_tail(sA[qg], 0);
+        if (tl.masked(tl.at(0))) mask_tail(sA[qg], tl.at(0));
         const float mx = row_max(sA[qg]);
         m_ref[qg] = mx;
 #pragma unroll
@@ -506,8 +554,8 @@ void fa_fwd_bf16_kernel(FaArgs a) {
                 if (qg == 0) {
                     if (i < S::KCH) store_k_chunk(kw, i);
                     else if (i < S::KCH + 4) store_v_row(vw, i - S::KCH);
-                    else if (i == S::KCH + 4) load_k(t + 4);
-                    else if (i == S::KCH + 5) load_v(t + 2);
+                    else if (i == S::KCH + 4) load_k(tl.at(t + 4));
+                    else if (i == S::KCH + 5) load_v(tl.at(t + 2));
                 }
                 if (i < NY / 2) {
 #pragma unroll
@@ -535,12 +583,12 @@ void fa_fwd_bf16_kernel(FaArgs a) {
             need = need || mx_next[qg] > FA_LAZY_LOG2;
         }
         __syncthreads();
-        // ---- the last real tile: keys past the end take no weight
-        if (t + 1 == nt - 1 && tail) {
+        // ---- keys past the end or padded take no weight
+        if (t + 1 < nt && tl.masked(tl.at(t + 1))) {
             need = false;
 #pragma unroll
             for (int qg = 0; qg < QG; ++qg) {
-                mask_tail(sn[qg], t + 1);
+                mask_tail(sn[qg], tl.at(t + 1));
                 mx_next[qg] = row_max(sn[qg]);
                 need = need || mx_next[qg] > FA_LAZY_LOG2;
             }
@@ -626,6 +674,7 @@ __device__ __forceinline__ bf16x4_t lds_read_tr(const lds_u8* p) {
 
 constexpr int FAD_WAVES = 8;
 
+template <bool PAD>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * FAD_WAVES, 64 * FAD_WAVES),
                           amdgpu_waves_per_eu(2, 2)))
 void fa_fwd_bf16_dma_kernel(FaArgs a) {
@@ -650,7 +699,8 @@ void fa_fwd_bf16_dma_kernel(FaArgs a) {
     const uint16_t* kb = a.k + kv_off;
     const uint16_t* vb = a.v + kv_off;
     const int64_t nq = a.nq, nk = a.nk;
-    const int nt = (int)((nk + FA_BC - 1) / FA_BC);
+    const FaTiles<PAD> tl(a, b);
+    const int nt = tl.nt;
 
     const int64_t qi = (int64_t)qt * BR + wave * 32 + l32;
     bf16x8_t qf[NKK];
@@ -726,8 +776,8 @@ void fa_fwd_bf16_dma_kernel(FaArgs a) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             const int64_t key = kv0 + 8 * (i >> 2) + 4 * g + (i & 3);
-            if (key >= nk) s0[i] = -__builtin_inff();
-            if (key + 32 >= nk) s1[i] = -__builtin_inff();
+            if (tl.dead(key)) s0[i] = -__builtin_inff();
+            if (tl.dead(key + 32)) s1[i] = -__builtin_inff();
         }
     };
     auto row_max = [&](const f32x16_t& s0, const f32x16_t& s1) {
@@ -742,18 +792,18 @@ void fa_fwd_bf16_dma_kernel(FaArgs a) {
     for (int i = 0; i < NDB; ++i) acc[i] = f32x16_t{};
     f32x16_t negm = f32x16_t{};   // -m in every slot: the C operand of the first k-step
     float m_ref, l_run = 0.f, mx_next = 0.f;
-    const bool tail = (nk % FA_BC) != 0;
 
-    // ---- prologue: K(0..2), V(0..1) into LDS; S(0); m from tile 0
+    // ---- prologue: K(0..2), V(0..1) into LDS; S(0); m from tile 0 (step
+    // indices; tl.at maps them to key tiles)
     // S tiles rotate through three register blocks: step t reads S(t) from
     // (x, y) and writes S(t+1) to (z, x), since the first half of S(t) is
     // consumed before the second half of S(t+1) is started.
     f32x16_t s0, s1, s2;
-    dma(kb, 0, kbuf(0));
-    dma(kb, 1, kbuf(1));
-    dma(kb, 2, kbuf(2));
-    dma(vb, 0, vbuf(0));
-    dma(vb, 1, vbuf(1));
+    dma(kb, tl.at(0), kbuf(0));
+    dma(kb, tl.at(1), kbuf(1));
+    dma(kb, tl.at(2), kbuf(2));
+    dma(vb, tl.at(0), vbuf(0));
+    dma(vb, tl.at(1), vbuf(1));
     __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0): this wave's tiles have landed
     __syncthreads();
 #pragma unroll
@@ -762,7 +812,7 @@ void fa_fwd_bf16_dma_kernel(FaArgs a) {
         s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfrag(0, NKK + kk), qf[kk], kk == 0 ? negm : s1, 0, 0, 0);
     }
     __syncthreads();              // K buffer 0 is refilled in the first iteration
-    if (nt == 1 && tail) mask_tail(s0, s1, 0);
+    if (tl.masked(tl.at(0))) mask_tail(s0, s1, tl.at(0));
     {
         const float mx = row_max(s0, s1);
         m_ref = mx;
@@ -806,7 +856,7 @@ void fa_fwd_bf16_dma_kernel(FaArgs a) {
                 pw[w] = pack_bf16x2(p0, p1);
             }
             // K(t+3) where K(t) was, one request every NX / NI groups
-            if (i % (NX / NI) == 0) dma_one(kb, t + 3, kbuf(j0), i / (NX / NI));
+            if (i % (NX / NI) == 0) dma_one(kb, tl.at(t + 3), kbuf(j0), i / (NX / NI));
             if (i + 2 == NX) vf[0] = vfrag(j0, 0);
             if (i + 1 == NX) vf[1] = vfrag(j0, 1);
             __builtin_amdgcn_sched_barrier(0);
@@ -824,7 +874,7 @@ void fa_fwd_bf16_dma_kernel(FaArgs a) {
             if (i + 2 < NY) vf[(i + 2) % 3] = vfrag(j0, i + 2);
             acc[i / 4] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i % 3], pb[i % 4], acc[i / 4], 0, 0, 0);
             // V(t+2) where V(t-1) was, one request every NY / NI groups
-            if (i % (NY / NI) == 0) dma_one(vb, t + 2, vbuf(j2), i / (NY / NI));
+            if (i % (NY / NI) == 0) dma_one(vb, tl.at(t + 2), vbuf(j2), i / (NY / NI));
             if (i < NY / 2) {
 #pragma unroll
                 for (int e = 0; e < SPM; ++e)
@@ -849,9 +899,9 @@ void fa_fwd_bf16_dma_kernel(FaArgs a) {
         __syncthreads();
         kf[0] = kfrag(j2, 0);
         kf[1] = kfrag(j2, 1);
-        // ---- the last real tile: keys past the end take no weight
-        if (t + 1 == nt - 1 && tail) {
-            mask_tail(sn0, sn1, t + 1);
+        // ---- keys past the end or padded take no weight
+        if (t + 1 < nt && tl.masked(tl.at(t + 1))) {
+            mask_tail(sn0, sn1, tl.at(t + 1));
             mx_next = row_max(sn0, sn1);
         }
         // ---- lazy rescale for S(t+1) (rare after the first tiles)
@@ -930,6 +980,7 @@ void fa_fwd_f32_kernel(FaArgs a) {
     const float* kbp = (const float*)a.k + kv_off;
     const float* vbp = (const float*)a.v + kv_off;
     const int64_t nq = a.nq, nk = a.nk;
+    const int64_t plo = a.has_pad ? a.pad_lo[b] : 0, phi = a.has_pad ? a.pad_hi[b] : 0;
 
     const int part = tid % TPQ;
     const int64_t qi = (int64_t)qt * QPB + tid / TPQ;
@@ -983,6 +1034,7 @@ void fa_fwd_f32_kernel(FaArgs a) {
         __syncthreads();
         const int cnt = (int)((nk - kv0) < FA32_BC ? (nk - kv0) : FA32_BC);
         for (int j = 0; j < cnt; ++j) {
+            if (kv0 + j >= plo && kv0 + j < phi) continue;   // padded key
             const float* kr = ks + j * D + part * 32;
             float s = 0.f;
 #pragma unroll
@@ -1020,9 +1072,15 @@ int flash_attn_rows_per_workgroup(bool bf16, int64_t head_dim) {
 
 hipError_t launch_flash_attn(const void* q, const void* k, const void* v, void* o, float* lse,
                              int64_t batch, int64_t nq, int64_t nk, int64_t heads,
-                             int64_t head_dim, float scale, const RopeArgs* rope, bool bf16,
-                             hipStream_t st) {
+                             int64_t head_dim, float scale, const RopeArgs* rope,
+                             const int32_t* key_pad, bool bf16, hipStream_t st) {
     FaArgs a;
+    a.has_pad = key_pad != nullptr;
+    for (int i = 0; i < FA_MAX_PAD_BATCH; ++i) {
+        const bool in = key_pad != nullptr && i < batch;
+        a.pad_lo[i] = in ? key_pad[2 * i] : 0;
+        a.pad_hi[i] = in ? key_pad[2 * i + 1] : 0;
+    }
     a.q = (const uint16_t*)q;
     a.k = (const uint16_t*)k;
     a.v = (const uint16_t*)v;
@@ -1046,8 +1104,15 @@ hipError_t launch_flash_attn(const void* q, const void* k, const void* v, void* 
     const dim3 grid((unsigned)a.total_tiles);
     if (bf16) {
         const dim3 block(64 * FA_WAVES);
-        if (head_dim == 128) hipLaunchKernelGGL(fa_fwd_bf16_dma_kernel, grid, dim3(64 * FAD_WAVES), 0, st, a);
-        else hipLaunchKernelGGL((fa_fwd_bf16_kernel<64, FA_WAVES, FA_QG>), grid, block, 0, st, a);
+        const dim3 dblock(64 * FAD_WAVES);
+        if (head_dim == 128 && a.has_pad)
+            hipLaunchKernelGGL(fa_fwd_bf16_dma_kernel<true>, grid, dblock, 0, st, a);
+        else if (head_dim == 128)
+            hipLaunchKernelGGL(fa_fwd_bf16_dma_kernel<false>, grid, dblock, 0, st, a);
+        else if (a.has_pad)
+            hipLaunchKernelGGL((fa_fwd_bf16_kernel<64, FA_WAVES, FA_QG, true>), grid, block, 0, st, a);
+        else
+            hipLaunchKernelGGL((fa_fwd_bf16_kernel<64, FA_WAVES, FA_QG, false>), grid, block, 0, st, a);
     } else {
         const dim3 block(256);
         if (head_dim == 128) hipLaunchKernelGGL(fa_fwd_f32_kernel<128>, grid, block, 0, st, a);

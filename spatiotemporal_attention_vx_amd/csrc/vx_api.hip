@@ -23,8 +23,9 @@ hipError_t launch_rope3d(void* q, void* k, int64_t batch, int64_t n_tokens, int6
                          int64_t head_dim, const RopeArgs& r, bool bf16, hipStream_t st);
 hipError_t launch_flash_attn(const void* q, const void* k, const void* v, void* o, float* lse,
                              int64_t batch, int64_t nq, int64_t nk, int64_t heads,
-                             int64_t head_dim, float scale, const RopeArgs* rope, bool bf16,
-                             hipStream_t st);
+                             int64_t head_dim, float scale, const RopeArgs* rope,
+                             const int32_t* key_pad, bool bf16, hipStream_t st);
+constexpr int FA_MAX_PAD_BATCH = 64;
 hipError_t launch_attn_merge(const void* oa, const float* lsea, const void* ob, const float* lseb,
                              void* o, float* lse, int64_t batch, int64_t n, int64_t heads,
                              int64_t head_dim, bool bf16, hipStream_t st);
@@ -169,7 +170,8 @@ int adaln(const char* fn, const void* x, const void* shift, const void* scale, v
 // self-attention one.
 int flash_attn(const char* fn, const void* q, const void* k, const void* v, void* o, float* lse,
                int64_t batch, int64_t nq, int64_t nk, int64_t heads, int64_t head_dim,
-               float softmax_scale, const vx_rope3d_desc* rope_q, int dt, void* hip_stream) {
+               float softmax_scale, const vx_rope3d_desc* rope_q, const int32_t* key_pad, int dt,
+               void* hip_stream) {
     if (!q || !k || !v || !o) return fail(VX_ERR_NULL, "%s: NULL tensor", fn);
     if (int e = check_dtype(fn, dt)) return e;
     if (batch <= 0 || nq <= 0 || nk <= 0 || heads <= 0 || head_dim <= 0)
@@ -181,6 +183,18 @@ int flash_attn(const char* fn, const void* q, const void* k, const void* v, void
     vx::RopeArgs r;
     if (rope_q)
         if (int e = check_rope(fn, rope_q, nq, head_dim, &r)) return e;
+    if (key_pad) {
+        if (batch > vx::FA_MAX_PAD_BATCH)
+            return fail(VX_ERR_UNSUPPORTED, "%s: key padding serves batch <= %d, not %lld", fn,
+                        vx::FA_MAX_PAD_BATCH, (long long)batch);
+        for (int64_t i = 0; i < batch; ++i) {
+            const int64_t lo = key_pad[2 * i], hi = key_pad[2 * i + 1];
+            if (lo < 0 || hi < lo || hi > nk || hi - lo >= nk)
+                return fail(VX_ERR_INVALID, "%s: key_pad[%lld] = [%lld, %lld) must satisfy "
+                            "0 <= lo <= hi <= n_kv and leave a valid key (n_kv = %lld)", fn,
+                            (long long)i, (long long)lo, (long long)hi, (long long)nk);
+        }
+    }
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
         (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)))
         return fail(VX_ERR_ALIGN, "%s: q, k, v, o must be 16-byte aligned, lse 4-byte", fn);
@@ -200,7 +214,8 @@ int flash_attn(const char* fn, const void* q, const void* k, const void* v, void
         return fail(VX_ERR_INVALID, "%s: lse overlaps a tensor", fn);
     const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)head_dim);
     return launched(vx::launch_flash_attn(q, k, v, o, lse, batch, nq, nk, heads, head_dim, scale,
-                                          rope_q ? &r : nullptr, bf16, (hipStream_t)hip_stream),
+                                          rope_q ? &r : nullptr, key_pad, bf16,
+                                          (hipStream_t)hip_stream),
                     fn);
 }
 
@@ -252,7 +267,7 @@ int vx_flash_attn_fwd(const void* q, const void* k, const void* v, void* o, floa
                       float softmax_scale, const vx_rope3d_desc* rope_q, int dt,
                       void* hip_stream) {
     return flash_attn("vx_flash_attn_fwd", q, k, v, o, lse, batch, n_tokens, n_tokens, heads,
-                      head_dim, softmax_scale, rope_q, dt, hip_stream);
+                      head_dim, softmax_scale, rope_q, nullptr, dt, hip_stream);
 }
 
 int vx_flash_attn_fwd_kv(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -260,7 +275,16 @@ int vx_flash_attn_fwd_kv(const void* q, const void* k, const void* v, void* o, f
                          int64_t head_dim, float softmax_scale, const vx_rope3d_desc* rope_q,
                          int dt, void* hip_stream) {
     return flash_attn("vx_flash_attn_fwd_kv", q, k, v, o, lse, batch, n_q, n_kv, heads, head_dim,
-                      softmax_scale, rope_q, dt, hip_stream);
+                      softmax_scale, rope_q, nullptr, dt, hip_stream);
+}
+
+int vx_flash_attn_fwd_masked(const void* q, const void* k, const void* v, void* o, float* lse,
+                             int64_t batch, int64_t n_q, int64_t n_kv, int64_t heads,
+                             int64_t head_dim, float softmax_scale, const vx_rope3d_desc* rope_q,
+                             const int32_t* key_pad, int dt, void* hip_stream) {
+    if (!key_pad) return fail(VX_ERR_NULL, "vx_flash_attn_fwd_masked: key_pad NULL");
+    return flash_attn("vx_flash_attn_fwd_masked", q, k, v, o, lse, batch, n_q, n_kv, heads,
+                      head_dim, softmax_scale, rope_q, key_pad, dt, hip_stream);
 }
 
 int vx_attn_merge2(const void* o_a, const float* lse_a, const void* o_b, const float* lse_b,

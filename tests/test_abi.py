@@ -190,6 +190,26 @@ def test_attention_kv_rejects(ptrs, nq, nk, d, rope, code):
 
 
 @host_only
+@pytest.mark.parametrize("batch,nk,pads,code", [
+    (1, 30, None, NULL),
+    (1, 30, [(-1, 5)], INVALID),
+    (1, 30, [(6, 5)], INVALID),
+    (1, 30, [(0, 31)], INVALID),
+    (1, 30, [(0, 30)], INVALID),            # no valid key left
+    (2, 30, [(0, 29), (3, 40)], INVALID),
+    (65, 30, [(0, 1)] * 65, UNSUPPORTED),
+])
+def test_attention_masked_rejects(batch, nk, pads, code):
+    lib = binding.load()
+    arr = None
+    if pads is not None:
+        arr = (ctypes.c_int32 * (2 * len(pads)))(*[x for p in pads for x in p])
+    assert lib.vx_flash_attn_fwd_masked(A, A + 64 * MB, A + 128 * MB, A + 192 * MB, None, batch,
+                                        24, nk, 2, 64, 0.0, None, arr, 1, None) == code
+    assert lib.vx_last_error().decode().startswith("vx_flash_attn_fwd_masked")
+
+
+@host_only
 @pytest.mark.parametrize("ptrs,n,d,dt,code", [
     ((None, A + MB, A + 2 * MB, A + 3 * MB, A + 4 * MB, A + 5 * MB), 24, 64, 1, NULL),
     ((A, None, A + 2 * MB, A + 3 * MB, A + 4 * MB, A + 5 * MB), 24, 64, 1, NULL),

@@ -184,3 +184,39 @@ def test_merge_with_empty_part_and_with_itself():
     mo, ml = oracle.merge_lse(o, lse, o, lse)      # the same keys twice: Z doubles
     np.testing.assert_allclose(mo, o, rtol=0, atol=1e-14)
     np.testing.assert_allclose(ml, lse + np.log(2.0), rtol=0, atol=1e-13)
+
+
+# ---- key padding
+
+@pytest.mark.parametrize("lo,hi", [(0, 10), (5, 17), (30, 40), (0, 39), (12, 12)])
+def test_masked_matches_library_sdpa_with_bool_mask(lo, hi):
+    q, k, v = _qkv(40, 2, 64, seed=16)
+    o, lse = oracle.attention_masked(q, k, v, lo, hi)
+    allow = np.ones((40, 40), dtype=bool)
+    allow[:, lo:hi] = False
+    t = lambda a: torch.from_numpy(a).permute(1, 0, 2)[None]
+    ref = torch.nn.functional.scaled_dot_product_attention(t(q), t(k), t(v),
+                                                           attn_mask=torch.from_numpy(allow))
+    np.testing.assert_allclose(o, ref[0].permute(1, 0, 2).numpy(), rtol=0, atol=1e-12)
+    s = np.einsum("qhd,khd->hqk", q, k) / 8.0
+    s[:, :, lo:hi] = -np.inf
+    np.testing.assert_allclose(lse, scipy.special.logsumexp(s, axis=-1), rtol=0, atol=1e-12)
+
+
+def test_masked_keys_do_not_matter():
+    q, k, v = _qkv(50, 2, 64, seed=17)
+    o1, l1 = oracle.attention_masked(q, k, v, 20, 35)
+    k2, v2 = k.copy(), v.copy()
+    k2[20:35] *= -7.0
+    v2[20:35] += 100.0
+    o2, l2 = oracle.attention_masked(q, k2, v2, 20, 35)
+    np.testing.assert_array_equal(o1, o2)
+    np.testing.assert_array_equal(l1, l2)
+
+
+def test_mask_leaving_one_key_returns_its_value():
+    q, k, v = _qkv(9, 2, 64, seed=18)
+    o, _ = oracle.attention_masked(q, k, v, 1, 9)
+    np.testing.assert_array_equal(o, np.broadcast_to(v[0], o.shape))
+    with pytest.raises(ValueError):
+        oracle.attention_masked(q, k, v, 0, 9)
