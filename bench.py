@@ -56,6 +56,9 @@ def parse():
                    help="AdaLN variant in the step: table layout and storage types")
     p.add_argument("--pairing", type=int, choices=[0, 1, 2], default=None,
                    help="RoPE pairing override (0 adjacent, 1 head halves, 2 band halves)")
+    p.add_argument("--kv-split", type=int, default=0,
+                   help="run attention as two key parts [0, S) and [S, N) merged through their "
+                        "LSEs (vx_flash_attn_fwd_kv twice + vx_attn_merge2); 0 = one call")
     p.add_argument("--cpu-rows", type=int, default=512,
                    help="query rows of the oracle CPU baseline (0 = skip it)")
     p.add_argument("--copy-calibration", action="store_true",
@@ -66,16 +69,20 @@ def parse():
 def attention_kernel_name(wl):
     if wl.dtype != "bf16":
         return f"fa_fwd_f32_kernel<{wl.head_dim}>"
-    return "fa_fwd_bf16_dma_kernel" if wl.head_dim == 128 else f"fa_fwd_bf16_kernel<{wl.head_dim}, 8, 1>"
+    if wl.head_dim == 128:
+        return "fa_fwd_bf16_dma_kernel<false>"
+    return f"fa_fwd_bf16_kernel<{wl.head_dim}, 8, 1, false>"
 
 
-def measured_traffic(wl):
+def measured_traffic(wl, args, pairing):
     """HBM bytes per attention launch from the committed rocprofv3 FETCH_SIZE /
     WRITE_SIZE record (scaled by the copy calibration), or None when the record
-    is for another workload or the kernel source has changed since."""
+    is for another workload or launch (it was taken with one attention call, Q
+    rotated on load, adjacent RoPE pairs) or the kernel source has changed since."""
     import hashlib
     path = os.path.join(ROOT, "profiles", "attention_large_traffic.json")
-    if wl.name != "large" or not os.path.exists(path):
+    if (wl.name != "large" or args.kv_split or args.rope != "fused" or pairing != 0
+            or not os.path.exists(path)):
         return None
     with open(path) as f:
         rec = json.load(f)
@@ -158,10 +165,26 @@ def main():
     fused = args.rope == "fused"
     stream = torch.cuda.current_stream()
 
-    ev = {name: [] for name in ("adaln", "rope", "attn")}
+    ev = {name: [] for name in ("adaln", "rope", "attn", "merge")}
+    split = args.kv_split
+    if split:
+        if not 0 < split < wl.n_tokens or wl.batch != 1:
+            raise SystemExit(f"--kv-split needs 0 < S < {wl.n_tokens} and batch 1")
+        parts = [(torch.empty_like(tq), torch.empty((1, wl.heads, wl.n_tokens), device=dev))
+                 for _ in range(2)]
+        keys = [(tk[:, :split], tv[:, :split]), (tk[:, split:], tv[:, split:])]
+
+    def attention():
+        if not split:
+            binding.flash_attn_fwd(tq, tk, tv, to, None, 0.0, desc if fused else None,
+                                   stream=stream)
+            return
+        for (o_p, l_p), (k_p, v_p) in zip(parts, keys):
+            binding.flash_attn_fwd_kv(tq, k_p, v_p, o_p, l_p, 0.0, desc if fused else None,
+                                      stream=stream)
 
     def step(record):
-        marks = [torch.cuda.Event(enable_timing=True) for _ in range(4)] if record else None
+        marks = [torch.cuda.Event(enable_timing=True) for _ in range(5)] if record else None
         if record:
             marks[0].record(stream)
         if args.adaln == "token":
@@ -173,12 +196,18 @@ def main():
         binding.rope3d_apply(None if fused else tq, tk, desc, stream=stream)
         if record:
             marks[2].record(stream)
-        binding.flash_attn_fwd(tq, tk, tv, to, None, 0.0, desc if fused else None, stream=stream)
+        attention()
         if record:
             marks[3].record(stream)
+        if split:
+            (oa, la), (ob, lb) = parts
+            binding.attn_merge2(oa, la, ob, lb, to, None, stream=stream)
+        if record:
+            marks[4].record(stream)
             ev["adaln"].append((marks[0], marks[1]))
             ev["rope"].append((marks[1], marks[2]))
             ev["attn"].append((marks[2], marks[3]))
+            ev["merge"].append((marks[3], marks[4]))
 
     for _ in range(args.warmup):
         step(False)
@@ -198,7 +227,7 @@ def main():
         del src, dst
 
     ms = {kname: float(np.mean([a.elapsed_time(b) for a, b in pairs]))
-          for kname, pairs in ev.items()}
+          for kname, pairs in ev.items() if pairs}
     ms_step = wall * 1e3 / args.steps
     flops = wl.attn_flops()
     value = flops / (ms_step * 1e-3) / 1e12
@@ -218,6 +247,16 @@ def main():
         "rope_gbs": round(rope_bytes / (ms["rope"] * 1e-3) / 1e9, 1),
         "rope_hbm_frac": round(rope_bytes / (ms["rope"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
     }
+    if split:
+        # o_a, o_b and both LSEs read, o written
+        o_bytes = to.numel() * to.element_size()
+        merge_bytes = 3 * o_bytes + 2 * parts[0][1].numel() * 4
+        kernels.update({
+            "kv_split": split,
+            "merge_ms": round(ms["merge"], 4),
+            "merge_gbs": round(merge_bytes / (ms["merge"] * 1e-3) / 1e9, 1),
+            "merge_hbm_frac": round(merge_bytes / (ms["merge"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+        })
     record = {
         "metric": METRIC if wl.name == configs.BENCH_WORKLOAD else
         (f"flash-attn TFLOP/s + % bf16 MFMA peak at {wl.n_tokens:,} tokens, "
@@ -251,7 +290,7 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
-            "traffic": measured_traffic(wl),
+            "traffic": measured_traffic(wl, args, pairing),
             "kernel": attention_kernel_name(wl),
         },
         "kernels": kernels,

@@ -86,7 +86,7 @@ WORKLOADS = {
 # One GPU's share of a workload under Ulysses sequence parallelism over P
 # GPUs (vidax paper §2 "Spatiotemporal tensor and sequence sharding": tokens
 # are sharded for the per-token work, an all-to-all regathers the sequence
-# and shards the heads for attention; §3.1 Table 1 runs Wan2.2 A14B with
+# and shards the heads for attention; §4, Table 2 runs Wan2.2 A14B with
 # SP 2 and CogVideoX1.5 with SP 4).  A GPU then attends over all N tokens
 # with H/P heads (RoPE is applied in that layout too, where every token's
 # grid position is global) and modulates ceil(N/P) tokens at the full model
