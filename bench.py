@@ -69,9 +69,7 @@ def parse():
 def attention_kernel_name(wl):
     if wl.dtype != "bf16":
         return f"fa_fwd_f32_kernel<{wl.head_dim}>"
-    if wl.head_dim == 128:
-        return "fa_fwd_bf16_dma_kernel<false>"
-    return f"fa_fwd_bf16_kernel<{wl.head_dim}, 8, 1, false>"
+    return f"fa_fwd_bf16_dma_kernel<{wl.head_dim}, false>"
 
 
 def measured_traffic(wl, args, pairing):

@@ -28,6 +28,11 @@
 //     over keys in the order the S^T accumulator hands them out, and the
 //     V^T fragments are read in that key order, so P never touches LDS.  The
 //     row sum is taken over the same rounded weights with v_dot2_f32_bf16.
+//   * K and V tiles go from global memory straight into LDS
+//     (buffer_load_dwordx4 ... lds), row-major with a per-row 16-byte chunk
+//     permutation, three buffers each; V^T fragments come from the
+//     transposing LDS read ds_read_b64_tr_b16.  A tile is 16 KiB: 64 keys at
+//     head_dim 128, 128 keys at head_dim 64, 32 MFMAs either way.
 //   * Software pipeline, one key tile t per iteration:
 //       X: S(t+1) = K(t+1) Q^T (MFMA)  interleaved with  exp/convert of S(t)
 //       Y: O += V(t)^T P(t)   (MFMA)  interleaved with  row sum of P(t),
@@ -35,13 +40,6 @@
 //     with the tile loads for later iterations spread over both phases and
 //     one barrier per tile.  Each MFMA and the work meant to run under it
 //     form a group that sched_barrier(0) keeps in order.
-//   * head_dim 128 (fa_fwd_bf16_dma_kernel): K and V tiles go from global
-//     memory straight into LDS (buffer_load_dwordx4 ... lds), row-major with
-//     a per-row 16-byte chunk permutation, three buffers each; V^T fragments
-//     come from the transposing LDS read ds_read_b64_tr_b16.
-//     head_dim 64 (fa_fwd_bf16_kernel): K and V tiles are staged through
-//     VGPRs; V is transposed in registers and stored as V^T with an XOR
-//     chunk permutation, K with padded rows.
 //   * Tiles past the sequence end are read through a buffer resource that
 //     ends at the sequence end, so they load as zeros with no per-lane test;
 //     scores of keys past the end are set to -inf in the last real tile.
@@ -59,12 +57,6 @@
 
 #include "vx_device.h"
 
-#ifndef VX_FA_WAVES
-#define VX_FA_WAVES 8
-#endif
-#ifndef VX_FA_QG
-#define VX_FA_QG 1
-#endif
 
 
 namespace vx {
@@ -97,7 +89,6 @@ struct FaArgs {
 
 // ---------------------------------------------------------------- bf16 MFMA
 
-constexpr int FA_BC = 64;    // keys per tile
 
 // Key-tile order of one (batch, head).  Without key padding (PAD false)
 // tiles run 0 .. nt - 1 and only the last can hold dead keys (past the
@@ -106,18 +97,18 @@ constexpr int FA_BC = 64;    // keys per tile
 // tile holding key pad_hi, so the first tile always has a valid key and the
 // running maximum starts finite.  Step indices at or past nt (prefetches
 // beyond the last step) map to themselves and load as zeros.
-template <bool PAD>
+template <bool PAD, int BC>
 struct FaTiles {
     int nt, t0;
-    int64_t nk, lo, hi;
+    int nk, lo, hi;   // the host keeps token counts below 2^31
     bool tail;
     __device__ FaTiles(const FaArgs& a, int64_t b) {
-        nk = a.nk;
-        nt = (int)((nk + FA_BC - 1) / FA_BC);
+        nk = (int)a.nk;
+        nt = (int)((nk + BC - 1) / BC);
         lo = PAD ? a.pad_lo[b] : 0;
         hi = PAD ? a.pad_hi[b] : 0;
-        t0 = (PAD && lo == 0 && hi > 0) ? (int)(hi / FA_BC) : 0;
-        tail = (nk % FA_BC) != 0;
+        t0 = (PAD && lo == 0 && hi > 0) ? hi / BC : 0;
+        tail = (nk % BC) != 0;
     }
     __device__ int at(int i) const {
         if constexpr (!PAD) return i;
@@ -127,42 +118,14 @@ struct FaTiles {
     // does tile tt hold a key past the end or a padded key
     __device__ bool masked(int tt) const {
         if constexpr (!PAD) return tail && tt == nt - 1;
-        const int64_t kv0 = (int64_t)tt * FA_BC;
-        return (tail && tt == nt - 1) || (kv0 < hi && kv0 + FA_BC > lo);
+        const int kv0 = tt * BC;
+        return (tail && tt == nt - 1) || (kv0 < hi && kv0 + BC > lo);
     }
-    __device__ bool dead(int64_t key) const {
+    __device__ bool dead(int key) const {
         if constexpr (!PAD) return key >= nk;
         return (key >= nk) | ((key >= lo) & (key < hi));
     }
 };
-constexpr int FA_PAD = 8;    // LDS row padding of K and V^T (elements)
-constexpr int FA_WAVES = VX_FA_WAVES;   // waves per workgroup
-constexpr int FA_QG = VX_FA_QG;         // 32-row query groups per wave
-
-typedef float f32x8_t __attribute__((ext_vector_type(8)));
-
-template <int D, int WAVES, int QG>
-struct FaShape {
-    static constexpr int NT = 64 * WAVES;            // threads per workgroup
-    static constexpr int BR = 32 * QG * WAVES;       // query rows per workgroup
-    static constexpr int KROW = D + FA_PAD;          // K row pitch in LDS
-    static constexpr int VROW = FA_BC + FA_PAD;      // V^T row pitch in LDS
-    static constexpr int KS = FA_BC * KROW;          // K tile elements
-    static constexpr int VS = D * VROW;              // V^T tile elements
-    static constexpr int KCH = FA_BC * D / 8 / NT;   // 16-byte K chunks per thread
-    static constexpr int DQ = D / 4;                 // V: 4-wide d groups
-    static constexpr int KPT = FA_BC * D / 4 / NT;   // V: keys per thread
-    static_assert(KCH >= 1 && KPT >= 2 && KPT % 2 == 0 && KPT <= 8, "tile does not divide");
-};
-
-// Key order inside each group of 16 keys as the S^T accumulator hands them
-// to the P^T operand: lanes 0-31 carry keys {0-3, 8-11}, lanes 32-63 carry
-// {4-7, 12-15}.  LDS position p of V^T holds key swap_bits23(p) (an
-// involution), so lane half g reads 8 contiguous elements at 8g.
-__device__ __forceinline__ int swap_bits23(int p) {
-    return (p & ~12) | ((p & 4) << 1) | ((p & 8) >> 1);
-}
-
 // {x[l % 32], x[l % 32 + 32]} in some order, for every lane l, through
 // v_permlane32_swap (no LDS round trip); max and sum are symmetric in them.
 __device__ __forceinline__ float half_max(float x) {
@@ -189,30 +152,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, 
 // The running maximum may trail a row's true maximum by up to this many
 // powers of two before the accumulator is rescaled (weights <= 2^8).
 constexpr float FA_LAZY_LOG2 = 8.0f;
-
-// V^T rows are stored with their 16-byte chunks permuted: chunk c of row r
-// sits at chunk c ^ vswz(r).  The transposing stores then write rows 4 apart
-// to 16 distinct bank groups, and a fragment read (16 consecutive rows, one
-// chunk) still covers every bank group once.
-__device__ __forceinline__ int vswz(int row) { return (row >> 4) & 3; }
-
-// Bytes {lo halves} or {hi halves} of two words, as one word: v_perm_b32.
-__device__ __forceinline__ uint32_t pick_lo16(uint32_t a0, uint32_t a1) {
-    return __builtin_amdgcn_perm(a1, a0, 0x05040100u);
-}
-__device__ __forceinline__ uint32_t pick_hi16(uint32_t a0, uint32_t a1) {
-    return __builtin_amdgcn_perm(a1, a0, 0x07060302u);
-}
-
-// Sum of the 8 bf16 values of v, added to acc (v_dot2_f32_bf16 against 1.0).
-__device__ __forceinline__ float sum_bf16x8(bf16x8_t v, float acc) {
-    const u32x4_t w = __builtin_bit_cast(u32x4_t, v);
-    const bf16x2_t one = {(__bf16)1.0f, (__bf16)1.0f};
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w[i]), one, acc, false);
-    return acc;
-}
 
 // Q fragment of one query row as the B operand of S^T = K Q^T: element
 // (ks, e) is column ks * 16 + g * 8 + e.  The row is optionally rotated by
@@ -300,370 +239,35 @@ __device__ __forceinline__ void load_q_fragment(const FaArgs& a, const uint16_t*
     }
 }
 
-template <int D, int WAVES, int QG, bool PAD>
-__global__ __attribute__((amdgpu_flat_work_group_size(64 * WAVES, 64 * WAVES),
-                          amdgpu_waves_per_eu(3 - QG, 3 - QG)))
-void fa_fwd_bf16_kernel(FaArgs a) {
-    using S = FaShape<D, WAVES, QG>;
-    constexpr int NKK = D / 16;      // MFMA k-steps of one S^T block
-    constexpr int NDB = D / 32;      // 32-row blocks of O^T
-    __shared__ __attribute__((aligned(16))) uint16_t lds[3 * S::KS + 2 * S::VS];
-    uint16_t* const kbuf[3] = {lds, lds + S::KS, lds + 2 * S::KS};
-    uint16_t* const vbuf[2] = {lds + 3 * S::KS, lds + 3 * S::KS + S::VS};
-
-    const int tid = threadIdx.x;
-    const int wave = tid >> 6, lane = tid & 63, l32 = lane & 31, g = lane >> 5;
-
-    const int64_t tile = xcd_remap(blockIdx.x, a.total_tiles);
-    const int qt = (int)(tile % a.n_qtiles);
-    const int64_t bh = tile / a.n_qtiles;
-    const int h = (int)(bh % a.heads);
-    const int64_t b = bh / a.heads;
-    const int64_t off = b * a.batch_stride + (int64_t)h * D;
-    const int64_t kv_off = b * a.kv_batch_stride + (int64_t)h * D;
-    const uint16_t* kb = a.k + kv_off;
-    const uint16_t* vb = a.v + kv_off;
-    const int64_t nq = a.nq, nk = a.nk;
-    const FaTiles<PAD> tl(a, b);
-    const int nt = tl.nt;
-
-    // query group qg of this wave: rows (wave * QG + qg) * 32 + l32 of the tile
-    int64_t qi[QG];
-    bf16x8_t qf[QG][NKK];
-#pragma unroll
-    for (int qg = 0; qg < QG; ++qg) {
-        qi[qg] = (int64_t)qt * S::BR + (wave * QG + qg) * 32 + l32;
-        load_q_fragment<D>(a, a.q + off, qi[qg], g, qf[qg]);
-    }
-
-    // ---- tile staging: global -> registers -> LDS.  Each thread's byte
-    // offsets inside a tile are fixed; the tile start and the sequence end
-    // live in a per-tile scalar buffer resource.
-    u32x4_t kreg[S::KCH];
-    uint2 vreg[S::KPT];
-    const int vdq = tid % S::DQ, vkg = tid / S::DQ;
-    const int64_t row_bytes = a.row_stride * 2;
-    uint32_t koff[S::KCH], voff[S::KPT];
-#pragma unroll
-    for (int i = 0; i < S::KCH; ++i) {
-        const int c = tid + S::NT * i;
-        koff[i] = (uint32_t)((c / (D / 8)) * row_bytes + (c % (D / 8)) * 16);
-    }
-#pragma unroll
-    for (int s = 0; s < S::KPT; ++s)
-        voff[s] = (uint32_t)(swap_bits23(vkg * S::KPT + s) * row_bytes + vdq * 8);
-
-    auto load_k = [&](int t) {
-        const int64_t kv0 = (int64_t)t * FA_BC;
-        const __amdgpu_buffer_rsrc_t r = buffer_rsrc(kb + kv0 * a.row_stride, (nk - kv0) * row_bytes);
-#pragma unroll
-        for (int i = 0; i < S::KCH; ++i) kreg[i] = __builtin_amdgcn_raw_buffer_load_b128(r, koff[i], 0, 0);
-    };
-    auto load_v = [&](int t) {
-        const int64_t kv0 = (int64_t)t * FA_BC;
-        const __amdgpu_buffer_rsrc_t r = buffer_rsrc(vb + kv0 * a.row_stride, (nk - kv0) * row_bytes);
-#pragma unroll
-        for (int s = 0; s < S::KPT; ++s) {
-            const auto w = __builtin_amdgcn_raw_buffer_load_b64(r, voff[s], 0, 0);
-            vreg[s] = uint2{w[0], w[1]};
-        }
-    };
-    auto store_k_chunk = [&](uint16_t* ks, int i) {
-        const int c = tid + S::NT * i;
-        *(u32x4_t*)(ks + (c / (D / 8)) * S::KROW + (c % (D / 8)) * 8) = kreg[i];
-    };
-    auto store_k = [&](uint16_t* ks) {
-#pragma unroll
-        for (int i = 0; i < S::KCH; ++i) store_k_chunk(ks, i);
-    };
-    // transpose: element j of each of the KPT keys -> one V^T row segment
-    auto store_v_row = [&](uint16_t* vt, int j) {
-        uint32_t w[S::KPT / 2];
-#pragma unroll
-        for (int s = 0; s < S::KPT; s += 2) {
-            const uint32_t a0 = (j < 2) ? vreg[s].x : vreg[s].y;
-            const uint32_t a1 = (j < 2) ? vreg[s + 1].x : vreg[s + 1].y;
-            w[s / 2] = (j & 1) ? pick_hi16(a0, a1) : pick_lo16(a0, a1);
-        }
-        const int row = vdq * 4 + j, pos = vkg * S::KPT;
-        uint16_t* dst = vt + row * S::VROW + (((pos >> 3) ^ vswz(row)) << 3) + (pos & 7);
-        if constexpr (S::KPT == 8) *(uint4*)dst = uint4{w[0], w[1], w[2], w[3]};
-        else if constexpr (S::KPT == 4) *(uint2*)dst = uint2{w[0], w[1]};
-        else *(uint32_t*)dst = w[0];
-    };
-    auto store_v = [&](uint16_t* vt) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) store_v_row(vt, j);
-    };
-
-    // S^T - m of one query group for both 32-key blocks of the tile at ks
-    auto scores = [&](f32x16_t* s, const uint16_t* ks, const bf16x8_t* q, const f32x16_t& negm) {
-#pragma unroll
-        for (int kb2 = 0; kb2 < 2; ++kb2) {
-#pragma unroll
-            for (int kk = 0; kk < NKK; ++kk) {
-                const bf16x8_t av = *(const bf16x8_t*)(ks + (kb2 * 32 + l32) * S::KROW + kk * 16 + g * 8);
-                s[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, q[kk], kk == 0 ? negm : s[kb2], 0, 0, 0);
-            }
-        }
-    };
-    auto mask_tail = [&](f32x16_t* s, int t) {
-        const int64_t kv0 = (int64_t)t * FA_BC;
-#pragma unroll
-        for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int64_t key = kv0 + kb2 * 32 + 8 * (i >> 2) + 4 * g + (i & 3);
-                if (tl.dead(key)) s[kb2][i] = -__builtin_inff();
-            }
-    };
-    auto row_max = [&](const f32x16_t* s) {
-        float mx = fmaxf(s[0][0], s[1][0]);
-#pragma unroll
-        for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-            for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[kb2][i]);
-        return half_max(mx);
-    };
-
-    f32x16_t acc[QG][NDB];
-    f32x16_t negm[QG];           // -m in every slot: the C operand of the first k-step
-    float m_ref[QG], l_run[QG], mx_next[QG];
-#pragma unroll
-    for (int qg = 0; qg < QG; ++qg) {
-#pragma unroll
-        for (int i = 0; i < NDB; ++i) acc[qg][i] = f32x16_t{};
-        negm[qg] = f32x16_t{};
-        l_run[qg] = 0.f;
-        mx_next[qg] = 0.f;
-    }
-    // ---- prologue: K(0), K(1), K(2) and V(0) into LDS; S(0); m from tile 0
-    // (step indices; tl.at maps them to key tiles)
-    f32x16_t sA[QG][2], sB[QG][2];
-    load_k(tl.at(0));
-    load_v(tl.at(0));
-    store_k(kbuf[0]);
-    store_v(vbuf[0]);
-    load_k(tl.at(1));
-    store_k(kbuf[1]);
-    load_k(tl.at(2));
-    store_k(kbuf[2]);
-    __syncthreads();
-#pragma unroll
-    for (int qg = 0; qg < QG; ++qg) scores(sA[qg], kbuf[0], qf[qg], negm[qg]);
-    __syncthreads();              // kbuf[0] is refilled in the first iteration
-    load_k(tl.at(3));
-    load_v(tl.at(1));
-#pragma unroll
-    for (int qg = 0; qg < QG; ++qg) {
-        if (tl.masked(tl.at(0))) mask_tail(sA[qg], tl.at(0));
-        const float mx = row_max(sA[qg]);
-        m_ref[qg] = mx;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            negm[qg][i] = -mx;
-            sA[qg][0][i] -= mx;
-            sA[qg][1][i] -= mx;
-        }
-    }
-
-    // Lane parts of the LDS fragment addresses.  K^T fragment i of a tile:
-    // rows (i / NKK) * 32 + l32, columns (i % NKK) * 16 + g * 8.  V^T
-    // fragment i: row (i / 4) * 32 + l32, 16-byte chunk 2 (i % 4) + g stored
-    // at chunk (2 (i % 4) + g) ^ vswz(row) = (2 (i % 4) ^ (2 (i / 4) & 3)) + (g ^ (l32 >> 4)).
-    const int klane = l32 * S::KROW + g * 8;
-    const int vlane = l32 * S::VROW + ((g ^ (l32 >> 4)) << 3);
-    auto kfrag = [&](const uint16_t* kt, int i) {
-        return *(const bf16x8_t*)(kt + klane + (i / NKK) * 32 * S::KROW + (i % NKK) * 16);
-    };
-    auto vfrag = [&](const uint16_t* vt, int i) {
-        const int db = i / 4, kk = i % 4;
-        return *(const bf16x8_t*)(vt + vlane + db * 32 * S::VROW + (((2 * kk) ^ ((2 * db) & 3)) << 3));
-    };
-    // K tiles rotate through three buffers (K(t+1) and K(t+2) are resident
-    // while K(t+3) is written), so the first K fragments of the next tile
-    // can be read before the barrier; V tiles use two.
-    bf16x8_t kf[3];
-    kf[0] = kfrag(kbuf[1], 0);
-    kf[1] = kfrag(kbuf[1], 1);
-
-    // One key tile.  sc holds S(t) - m (already rescaled), sn receives
-    // S(t+1).  The two halves are written out in issue order: every group
-    // below pairs one MFMA with the VALU, LDS and global-memory work that
-    // is to run under it, and sched_barrier(0) keeps the groups in order.
-    auto step = [&](f32x16_t (*sc)[2], f32x16_t (*sn)[2], int t) {
-        constexpr int NX = 2 * NKK;          // K fragments of S(t+1), each used by QG MFMAs
-        constexpr int WPM = 16 / NX;         // P words (2 weights) per group per fragment
-        constexpr int NY = NDB * FA_BC / 16; // V^T fragments of P V, each used by QG MFMAs
-        constexpr int MPM = 32 / (NY / 2);   // scores per group per fragment in the row max
-        constexpr int SPM = 16 / (NY / 2);   // P words per group per fragment in the row sum
-        const int k1 = (t + 1) % 3;
-        const uint16_t* kt = lds + k1 * S::KS;                          // K(t+1)
-        const uint16_t* kn = lds + (k1 == 2 ? 0 : k1 + 1) * S::KS;      // K(t+2)
-        uint16_t* kw = lds + (k1 == 0 ? 2 : k1 - 1) * S::KS;            // K(t+3), where K(t) was
-        const uint16_t* vt = lds + 3 * S::KS + (t & 1) * S::VS;         // V(t)
-        uint16_t* vw = lds + 3 * S::KS + ((t + 1) & 1) * S::VS;         // V(t+1)
-        // ---- X: S(t+1) = K(t+1) Q^T - m  ||  P(t) = 2^(S(t) - m)
-        bf16x8_t vf[3];
-        uint32_t pw[QG][16];
-#pragma unroll
-        for (int i = 0; i < NX; ++i) {
-            if (i + 2 < NX) kf[(i + 2) % 3] = kfrag(kt, i + 2);
-            const int kb2 = i / NKK, kk = i % NKK;
-#pragma unroll
-            for (int qg = 0; qg < QG; ++qg) {
-                sn[qg][kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                    kf[i % 3], qf[qg][kk], kk == 0 ? negm[qg] : sn[qg][kb2], 0, 0, 0);
-#pragma unroll
-                for (int e = 0; e < WPM; ++e) {
-                    const int w = i * WPM + e;   // weights 2w, 2w+1 of the group's 32 scores
-                    const float p0 = fast_exp2(sc[qg][(2 * w) >> 4][(2 * w) & 15]);
-                    const float p1 = fast_exp2(sc[qg][(2 * w + 1) >> 4][(2 * w + 1) & 15]);
-                    pw[qg][w] = pack_bf16x2(p0, p1);
-                }
-                if (qg == QG - 1 && i + 2 == NX) vf[0] = vfrag(vt, 0);
-                if (qg == QG - 1 && i + 1 == NX) vf[1] = vfrag(vt, 1);
-                __builtin_amdgcn_sched_barrier(0);
-            }
-        }
-        bf16x8_t pb[QG][FA_BC / 16];
-#pragma unroll
-        for (int qg = 0; qg < QG; ++qg)
-#pragma unroll
-            for (int kk = 0; kk < FA_BC / 16; ++kk)
-                pb[qg][kk] = __builtin_bit_cast(bf16x8_t, u32x4_t{pw[qg][4 * kk], pw[qg][4 * kk + 1],
-                                                                  pw[qg][4 * kk + 2], pw[qg][4 * kk + 3]});
-        // ---- Y: O += V(t)^T P(t)  ||  row sum of P(t); K(t+3), V(t+1) into
-        // LDS; loads of K(t+4), V(t+2); row max of S(t+1); first K(t+2) fragments
-        const bf16x2_t one = {(__bf16)1.0f, (__bf16)1.0f};
-        float mx[QG], psum[QG];
-#pragma unroll
-        for (int qg = 0; qg < QG; ++qg) {
-            mx[qg] = -__builtin_inff();
-            psum[qg] = l_run[qg];
-        }
-#pragma unroll
-        for (int i = 0; i < NY; ++i) {
-            if (i + 2 < NY) vf[(i + 2) % 3] = vfrag(vt, i + 2);
-            if (i + 2 == NY) kf[0] = kfrag(kn, 0);
-            if (i + 1 == NY) kf[1] = kfrag(kn, 1);
-#pragma unroll
-            for (int qg = 0; qg < QG; ++qg) {
-                acc[qg][i / 4] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i % 3], pb[qg][i % 4],
-                                                                         acc[qg][i / 4], 0, 0, 0);
-                if (qg == 0) {
-                    if (i < S::KCH) store_k_chunk(kw, i);
-                    else if (i < S::KCH + 4) store_v_row(vw, i - S::KCH);
-                    else if (i == S::KCH + 4) load_k(tl.at(t + 4));
-                    else if (i == S::KCH + 5) load_v(tl.at(t + 2));
-                }
-                if (i < NY / 2) {
-#pragma unroll
-                    for (int e = 0; e < SPM; ++e) {
-                        const int w = i * SPM + e;
-                        psum[qg] = __builtin_amdgcn_fdot2_f32_bf16(
-                            __builtin_bit_cast(bf16x2_t, pw[qg][w]), one, psum[qg], false);
-                    }
-                    __asm__ volatile("" ::"v"(psum[qg]));   // keep the row sum in this group
-                } else {
-#pragma unroll
-                    for (int e = 0; e < MPM; ++e) {
-                        const int j = (i - NY / 2) * MPM + e;
-                        mx[qg] = fmaxf(mx[qg], sn[qg][j >> 4][j & 15]);
-                    }
-                }
-                __builtin_amdgcn_sched_barrier(0);
-            }
-        }
-        bool need = false;
-#pragma unroll
-        for (int qg = 0; qg < QG; ++qg) {
-            l_run[qg] = psum[qg];
-            mx_next[qg] = half_max(mx[qg]);
-            need = need || mx_next[qg] > FA_LAZY_LOG2;
-        }
-        __syncthreads();
-        // ---- keys past the end or padded take no weight
-        if (t + 1 < nt && tl.masked(tl.at(t + 1))) {
-            need = false;
-#pragma unroll
-            for (int qg = 0; qg < QG; ++qg) {
-                mask_tail(sn[qg], tl.at(t + 1));
-                mx_next[qg] = row_max(sn[qg]);
-                need = need || mx_next[qg] > FA_LAZY_LOG2;
-            }
-        }
-        // ---- lazy rescale for S(t+1) (rare after the first tiles)
-        if (t + 1 < nt && __builtin_amdgcn_ballot_w64(need) != 0) {
-#pragma unroll
-            for (int qg = 0; qg < QG; ++qg) {
-                const float delta = fmaxf(mx_next[qg], 0.f);
-                const float alpha = fast_exp2(-delta);
-                m_ref[qg] += delta;
-                l_run[qg] *= alpha;
-#pragma unroll
-                for (int i = 0; i < NDB; ++i) acc[qg][i] *= alpha;
-                // -m is rewritten in place: a plain assignment here makes
-                // the register allocator copy the block on every tile.
-                const float nm = -m_ref[qg];
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    __asm__ volatile("v_mov_b32 %0, %1" : "+v"(negm[qg][i]) : "v"(nm));
-                    sn[qg][0][i] -= delta;
-                    sn[qg][1][i] -= delta;
-                }
-            }
-        }
-    };
-
-    for (int t = 0; t < nt; t += 2) {
-        step(sA, sB, t);
-        if (t + 1 >= nt) break;
-        step(sB, sA, t + 1);
-    }
-
-    // epilogue: combine the two halves' row sums, normalise, store
-#pragma unroll
-    for (int qg = 0; qg < QG; ++qg) {
-        const float l_tot = half_sum(l_run[qg]);
-        const float inv = 1.0f / l_tot;
-        if (qi[qg] < nq) {
-            uint16_t* ob = a.o + off + qi[qg] * a.row_stride;
-#pragma unroll
-            for (int db = 0; db < NDB; ++db)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const f32x16_t& c = acc[qg][db];
-                    uint2 w;
-                    w.x = pack_bf16x2(c[4 * r + 0] * inv, c[4 * r + 1] * inv);
-                    w.y = pack_bf16x2(c[4 * r + 2] * inv, c[4 * r + 3] * inv);
-                    *(uint2*)(ob + db * 32 + 8 * r + 4 * g) = w;
-                }
-            if (a.lse != nullptr && g == 0)
-                a.lse[bh * nq + qi[qg]] = (m_ref[qg] + __builtin_log2f(l_tot)) * 0.69314718055994531f;
-        }
-    }
-}
-
 // ---------------------------------------------------------------- bf16 MFMA, DMA staging
 //
-// Same computation and software pipeline as fa_fwd_bf16_kernel, for
-// head_dim 128, 8 waves and 256 query rows per workgroup, but the K and V
-// tiles go from global memory straight into LDS (buffer_load_dwordx4 ...
-// lds: one wave instruction moves 1 KiB, four 256-byte rows), so no VGPR
-// staging, no LDS store instructions and no register transpose.  Both tiles
-// are kept row-major in LDS, three buffers each, with the 16-byte chunks of
-// row r permuted by c -> c ^ dswz(r) (chosen by which global chunk each lane
-// fetches).  K fragments are plain 16-byte reads; V^T fragments for the
-// P V product come from ds_read_b64_tr_b16, which transposes 4 keys x 16
+// 8 waves and 256 query rows per workgroup.  The K and V tiles go from
+// global memory straight into LDS (buffer_load_dwordx4 ... lds: one wave
+// instruction moves 1 KiB), so no VGPR staging, no LDS store instructions
+// and no register transpose.  A tile is 16 KiB whatever the head dim: 64
+// keys at head_dim 128, 128 keys at head_dim 64, so both shapes issue 32
+// MFMAs per tile and pay the per-tile costs (barrier, DMA issue) equally;
+// head_dim 64 has twice the exponentials per MFMA.  Both tiles are kept
+// row-major in LDS, three buffers each, with the 16-byte chunks of row r
+// permuted by c -> c ^ swz(r) (chosen by which global chunk each lane
+// fetches).  K fragments are plain 16-byte reads; V^T fragments for the P V
+// product come from ds_read_b64_tr_b16, which transposes 4 keys x 16
 // head-dim columns across each 16-lane group: source lane s reads 4
 // consecutive columns of key s / 4, and lane i receives column i of the 4
 // keys.
 
-// chunk permutation of a 256-byte row: a bijection on 0..15 (16 consecutive
-// rows hit 16 distinct chunks), and 4 consecutive rows differ in bits 2-3
-// (4 rows x 4 aligned chunks hit 16 distinct chunks)
+// chunk permutation of a 256-byte row (head_dim 128): a bijection on 0..15
+// (16 consecutive rows hit 16 distinct chunks), and 4 consecutive rows
+// differ in bits 2-3 (4 rows x 4 aligned chunks hit 16 distinct chunks)
 __device__ __forceinline__ int dswz(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
+// chunk permutation of a 128-byte row (head_dim 64), where a row's parity
+// picks the half of the 256-byte bank window: among 16 consecutive rows the
+// 8 of each parity get distinct values (16 lanes on 16 rows hit 16 distinct
+// bank groups), and rows 4m and 4m + 2 differ in bit 2 (4 rows x 4 aligned
+// chunks hit 16 distinct bank groups)
+__device__ __forceinline__ int dswz64(int row) { return (((row >> 1) & 1) << 2) | ((row >> 2) & 3); }
+template <int D>
+__device__ __forceinline__ int dswz_d(int row) { return D == 128 ? dswz(row) : dswz64(row); }
 
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
@@ -674,14 +278,20 @@ __device__ __forceinline__ bf16x4_t lds_read_tr(const lds_u8* p) {
 
 constexpr int FAD_WAVES = 8;
 
-template <bool PAD>
+template <int D, bool PAD>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * FAD_WAVES, 64 * FAD_WAVES),
                           amdgpu_waves_per_eu(2, 2)))
 void fa_fwd_bf16_dma_kernel(FaArgs a) {
-    constexpr int D = 128, NKK = D / 16, NDB = D / 32;
+    constexpr int NKK = D / 16, NDB = D / 32;
+    constexpr int BC = 8192 / D;                      // keys per tile (a tile is 16 KiB)
+    constexpr int KB = BC / 32;                       // 32-key blocks of S^T per tile
+    constexpr int KS = BC / 16;                       // 16-key steps of P V per tile
+    constexpr int NSB = 3 * KB / 2;                   // S^T register blocks in rotation
     constexpr int BR = 32 * FAD_WAVES;                // query rows per workgroup
-    constexpr int ROWB = 2 * D;                       // bytes per K or V row (256)
-    constexpr int TILEB = FA_BC * ROWB;               // bytes per tile (16 KiB)
+    constexpr int ROWB = 2 * D;                       // bytes per K or V row
+    constexpr int CPR = ROWB / 16;                    // 16-byte chunks per row
+    constexpr int RPI = 1024 / ROWB;                  // rows per DMA instruction
+    constexpr int TILEB = BC * ROWB;                  // bytes per tile (16 KiB)
     constexpr int NI = TILEB / 1024 / FAD_WAVES;      // DMA instructions per wave per tensor (2)
     __shared__ __attribute__((aligned(1024))) uint8_t lds_raw[6 * TILEB];
     lds_u8* const lds = (lds_u8*)lds_raw;             // K buffers 0-2, V buffers 3-5
@@ -699,23 +309,23 @@ void fa_fwd_bf16_dma_kernel(FaArgs a) {
     const uint16_t* kb = a.k + kv_off;
     const uint16_t* vb = a.v + kv_off;
     const int64_t nq = a.nq, nk = a.nk;
-    const FaTiles<PAD> tl(a, b);
+    const FaTiles<PAD, BC> tl(a, b);
     const int nt = tl.nt;
 
     const int64_t qi = (int64_t)qt * BR + wave * 32 + l32;
     bf16x8_t qf[NKK];
     load_q_fragment<D>(a, a.q + off, qi, g, qf);
 
-    // ---- DMA: instruction m of this wave fills rows 4 I .. 4 I + 3 of the
-    // tile, I = wave * NI + m; lane L writes LDS bytes 16 L .. of that KiB,
-    // i.e. row 4 I + L / 16, chunk slot L % 16, which holds global chunk
-    // (L % 16) ^ dswz(row).
+    // ---- DMA: instruction m of this wave fills rows RPI I .. RPI I + RPI - 1
+    // of the tile, I = wave * NI + m; lane L writes LDS bytes 16 L .. of that
+    // KiB, i.e. row RPI I + L / CPR, chunk slot L % CPR, which holds global
+    // chunk (L % CPR) ^ swz(row).
     const int64_t row_bytes = a.row_stride * 2;
     uint32_t goff[NI];
 #pragma unroll
     for (int m = 0; m < NI; ++m) {
-        const int row = (wave * NI + m) * 4 + (lane >> 4);
-        goff[m] = (uint32_t)(row * row_bytes + (((lane & 15) ^ dswz(row)) << 4));
+        const int row = (wave * NI + m) * RPI + lane / CPR;
+        goff[m] = (uint32_t)(row * row_bytes + (((lane % CPR) ^ dswz_d<D>(row)) << 4));
     }
     const int swave = __builtin_amdgcn_readfirstlane(wave);   // wave-uniform, for M0
     // The DMA is written as inline assembly: with the builtin, the compiler
@@ -724,7 +334,7 @@ void fa_fwd_bf16_dma_kernel(FaArgs a) {
     // hand instead: an explicit vmcnt wait and the barrier publish a tile,
     // and no buffer is a DMA target while any wave may still read it.
     auto dma_one = [&](const uint16_t* base, int t, lds_u8* buf, int m) {
-        const int64_t kv0 = (int64_t)t * FA_BC;
+        const int64_t kv0 = (int64_t)t * BC;
         const __amdgpu_buffer_rsrc_t r = buffer_rsrc(base + kv0 * a.row_stride, (nk - kv0) * row_bytes);
         const uint32_t dst = (uint32_t)(uintptr_t)(buf + (swave * NI + m) * 1024);
         __asm__ volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
@@ -745,7 +355,7 @@ void fa_fwd_bf16_dma_kernel(FaArgs a) {
     // K fragment (kb2, kk): row kb2 * 32 + l32, chunk 2 kk + g
     uint32_t koff[NKK];
 #pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) koff[kk] = l32 * ROWB + (((2 * kk + g) ^ dswz(l32)) << 4);
+    for (int kk = 0; kk < NKK; ++kk) koff[kk] = l32 * ROWB + (((2 * kk + g) ^ dswz_d<D>(l32)) << 4);
     auto kfrag = [&](int jk, int i) {   // K buffer jk (compile-time), fragment i
         return *(const bf16x8_t*)(lds + koff[i % NKK] + (jk * TILEB + (i / NKK) * 32 * ROWB));
     };
@@ -761,29 +371,40 @@ void fa_fwd_bf16_dma_kernel(FaArgs a) {
             for (int db = 0; db < NDB; ++db) {
                 const int row = 4 * (2 * r + g) + (s_ >> 2);
                 const int chunk = 4 * db + 2 * hh + ((s_ & 3) >> 1);
-                voff[r][db] = 3 * TILEB + row * ROWB + ((chunk ^ dswz(row)) << 4) + (s_ & 1) * 8;
+                voff[r][db] = 3 * TILEB + row * ROWB + ((chunk ^ dswz_d<D>(row)) << 4) + (s_ & 1) * 8;
             }
     }
     auto vfrag = [&](int jv, int i) {   // V buffer jv (compile-time), fragment i
-        const int db = i / 4, kk = i % 4;
+        const int db = i / KS, kk = i % KS;
         const bf16x4_t lo = lds_read_tr(lds + voff[0][db] + (jv * TILEB + kk * 16 * ROWB));
         const bf16x4_t hi = lds_read_tr(lds + voff[1][db] + (jv * TILEB + kk * 16 * ROWB));
         return bf16x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     };
 
-    auto mask_tail = [&](f32x16_t& s0, f32x16_t& s1, int t) {
-        const int64_t kv0 = (int64_t)t * FA_BC;
+    // S^T of one tile is KB register blocks of 16 (32 keys each).  They
+    // rotate through NSB = 3 KB / 2 blocks: step J (= t % 3) reads S(t) from
+    // blocks (J KB + k) % NSB and writes S(t+1) to (J KB + KB + k) % NSB, so
+    // S(t+1)'s upper half takes the place of S(t)'s lower half, which the
+    // exponentials have consumed by then.
+    f32x16_t sb[NSB];
+    auto mask_tile = [&](auto jm, int t) {   // S(t) held in step jm's "next" blocks
+        constexpr int J = decltype(jm)::value;
+        const int kv0 = t * BC;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int64_t key = kv0 + 8 * (i >> 2) + 4 * g + (i & 3);
-            if (tl.dead(key)) s0[i] = -__builtin_inff();
-            if (tl.dead(key + 32)) s1[i] = -__builtin_inff();
-        }
+        for (int k = 0; k < KB; ++k)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int key = kv0 + k * 32 + 8 * (i >> 2) + 4 * g + (i & 3);
+                if (tl.dead(key)) sb[(J * KB + KB + k) % NSB][i] = -__builtin_inff();
+            }
     };
-    auto row_max = [&](const f32x16_t& s0, const f32x16_t& s1) {
-        float mx = fmaxf(s0[0], s1[0]);
+    auto row_max = [&](auto jm) {
+        constexpr int J = decltype(jm)::value;
+        float mx = sb[(J * KB + KB) % NSB][0];
 #pragma unroll
-        for (int i = 1; i < 16; ++i) mx = fmaxf(mx, fmaxf(s0[i], s1[i]));
+        for (int k = 0; k < KB; ++k)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sb[(J * KB + KB + k) % NSB][i]);
         return half_max(mx);
     };
 
@@ -793,12 +414,9 @@ void fa_fwd_bf16_dma_kernel(FaArgs a) {
     f32x16_t negm = f32x16_t{};   // -m in every slot: the C operand of the first k-step
     float m_ref, l_run = 0.f, mx_next = 0.f;
 
-    // ---- prologue: K(0..2), V(0..1) into LDS; S(0); m from tile 0 (step
-    // indices; tl.at maps them to key tiles)
-    // S tiles rotate through three register blocks: step t reads S(t) from
-    // (x, y) and writes S(t+1) to (z, x), since the first half of S(t) is
-    // consumed before the second half of S(t+1) is started.
-    f32x16_t s0, s1, s2;
+    // ---- prologue: K(0..2), V(0..1) into LDS; S(0) into blocks 0 .. KB-1
+    // (the "next" blocks of step J = 2); m from tile 0 (step indices; tl.at
+    // maps them to key tiles)
     dma(kb, tl.at(0), kbuf(0));
     dma(kb, tl.at(1), kbuf(1));
     dma(kb, tl.at(2), kbuf(2));
@@ -807,21 +425,22 @@ void fa_fwd_bf16_dma_kernel(FaArgs a) {
     __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0): this wave's tiles have landed
     __syncthreads();
 #pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) {
-        s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfrag(0, kk), qf[kk], kk == 0 ? negm : s0, 0, 0, 0);
-        s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfrag(0, NKK + kk), qf[kk], kk == 0 ? negm : s1, 0, 0, 0);
-    }
+    for (int k = 0; k < KB; ++k)
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk)
+            sb[k] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfrag(0, k * NKK + kk), qf[kk],
+                                                            kk == 0 ? negm : sb[k], 0, 0, 0);
     __syncthreads();              // K buffer 0 is refilled in the first iteration
-    if (tl.masked(tl.at(0))) mask_tail(s0, s1, tl.at(0));
+    if (tl.masked(tl.at(0))) mask_tile(std::integral_constant<int, 2>{}, tl.at(0));
     {
-        const float mx = row_max(s0, s1);
+        const float mx = row_max(std::integral_constant<int, 2>{});
         m_ref = mx;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            negm[i] = -mx;
-            s0[i] -= mx;
-            s1[i] -= mx;
-        }
+        for (int i = 0; i < 16; ++i) negm[i] = -mx;
+#pragma unroll
+        for (int k = 0; k < KB; ++k)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) sb[k][i] -= mx;
     }
     bf16x8_t kf[3];
     kf[0] = kfrag(1, 0);
@@ -830,27 +449,29 @@ void fa_fwd_bf16_dma_kernel(FaArgs a) {
     // Step t uses K buffers (t+1) % 3 (read), (t+2) % 3 (next tile's first
     // fragments), t % 3 (DMA target) and V buffers t % 3 (read), (t+2) % 3
     // (DMA target); the loop is unrolled three times so all are compile-time.
-    auto step = [&](auto tm, f32x16_t& sc0, f32x16_t& sc1, f32x16_t& sn0, f32x16_t& sn1, int t) {
-        constexpr int T3 = decltype(tm)::value;   // t % 3
-        constexpr int NX = 2 * NKK;          // K fragments (MFMAs) of S(t+1)
-        constexpr int WPM = 16 / NX;         // P words (2 weights) per MFMA
-        constexpr int NY = NDB * FA_BC / 16; // V^T fragments (MFMAs) of P V
-        constexpr int MPM = 32 / (NY / 2);   // scores per MFMA in the row max
-        constexpr int SPM = 16 / (NY / 2);   // P words per MFMA in the row sum
-        constexpr int j0 = T3, j1 = (T3 + 1) % 3, j2 = (T3 + 2) % 3;
+    auto step = [&](auto tm, int t) {
+        constexpr int J = decltype(tm)::value;   // t % 3
+        constexpr int NX = KB * NKK;          // K fragments (MFMAs) of S(t+1)
+        constexpr int WPM = 8 * KB / NX;      // P words (2 weights) per MFMA
+        constexpr int NY = NDB * KS;          // V^T fragments (MFMAs) of P V
+        constexpr int MPM = 16 * KB / (NY / 2);   // scores per MFMA in the row max
+        constexpr int SPM = 8 * KB / (NY / 2);    // P words per MFMA in the row sum
+        constexpr int j0 = J, j1 = (J + 1) % 3, j2 = (J + 2) % 3;
+        auto cur = [](int k) { return (J * KB + k) % NSB; };        // S(t) block k
+        auto nxt = [](int k) { return (J * KB + KB + k) % NSB; };   // S(t+1) block k
         // ---- X: S(t+1) = K(t+1) Q^T - m  ||  P(t) = 2^(S(t) - m)
         bf16x8_t vf[3];
-        uint32_t pw[16];
+        uint32_t pw[8 * KB];
 #pragma unroll
         for (int i = 0; i < NX; ++i) {
             if (i + 2 < NX) kf[(i + 2) % 3] = kfrag(j1, i + 2);
             const int kb2 = i / NKK, kk = i % NKK;
-            f32x16_t& d = kb2 ? sn1 : sn0;
+            f32x16_t& d = sb[nxt(kb2)];
             d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i % 3], qf[kk], kk == 0 ? negm : d, 0, 0, 0);
 #pragma unroll
             for (int e = 0; e < WPM; ++e) {
                 const int w = i * WPM + e;   // weights 2w, 2w+1: block (2w) / 16 of S(t)
-                const f32x16_t& src = (2 * w) < 16 ? sc0 : sc1;
+                const f32x16_t& src = sb[cur((2 * w) / 16)];
                 const float p0 = fast_exp2(src[(2 * w) & 15]);
                 const float p1 = fast_exp2(src[(2 * w + 1) & 15]);
                 pw[w] = pack_bf16x2(p0, p1);
@@ -861,9 +482,9 @@ void fa_fwd_bf16_dma_kernel(FaArgs a) {
             if (i + 1 == NX) vf[1] = vfrag(j0, 1);
             __builtin_amdgcn_sched_barrier(0);
         }
-        bf16x8_t pb[FA_BC / 16];
+        bf16x8_t pb[KS];
 #pragma unroll
-        for (int kk = 0; kk < FA_BC / 16; ++kk)
+        for (int kk = 0; kk < KS; ++kk)
             pb[kk] = __builtin_bit_cast(bf16x8_t, u32x4_t{pw[4 * kk], pw[4 * kk + 1], pw[4 * kk + 2], pw[4 * kk + 3]});
         // ---- Y: O += V(t)^T P(t)  ||  row sum of P(t); row max of S(t+1);
         // first K(t+2) fragments
@@ -872,7 +493,7 @@ void fa_fwd_bf16_dma_kernel(FaArgs a) {
 #pragma unroll
         for (int i = 0; i < NY; ++i) {
             if (i + 2 < NY) vf[(i + 2) % 3] = vfrag(j0, i + 2);
-            acc[i / 4] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i % 3], pb[i % 4], acc[i / 4], 0, 0, 0);
+            acc[i / KS] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i % 3], pb[i % KS], acc[i / KS], 0, 0, 0);
             // V(t+2) where V(t-1) was, one request every NY / NI groups
             if (i % (NY / NI) == 0) dma_one(vb, tl.at(t + 2), vbuf(j2), i / (NY / NI));
             if (i < NY / 2) {
@@ -885,7 +506,7 @@ void fa_fwd_bf16_dma_kernel(FaArgs a) {
 #pragma unroll
                 for (int e = 0; e < MPM; ++e) {
                     const int j = (i - NY / 2) * MPM + e;
-                    mx = fmaxf(mx, (j < 16 ? sn0 : sn1)[j & 15]);
+                    mx = fmaxf(mx, sb[nxt(j / 16)][j & 15]);
                 }
             }
             __builtin_amdgcn_sched_barrier(0);
@@ -901,8 +522,8 @@ void fa_fwd_bf16_dma_kernel(FaArgs a) {
         kf[1] = kfrag(j2, 1);
         // ---- keys past the end or padded take no weight
         if (t + 1 < nt && tl.masked(tl.at(t + 1))) {
-            mask_tail(sn0, sn1, tl.at(t + 1));
-            mx_next = row_max(sn0, sn1);
+            mask_tile(tm, tl.at(t + 1));
+            mx_next = row_max(tm);
         }
         // ---- lazy rescale for S(t+1) (rare after the first tiles)
         if (t + 1 < nt && __builtin_amdgcn_ballot_w64(mx_next > FA_LAZY_LOG2) != 0) {
@@ -916,20 +537,21 @@ void fa_fwd_bf16_dma_kernel(FaArgs a) {
             // register allocator copy the block on every tile.
             const float nm = -m_ref;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                __asm__ volatile("v_mov_b32 %0, %1" : "+v"(negm[i]) : "v"(nm));
-                sn0[i] -= delta;
-                sn1[i] -= delta;
-            }
+            for (int i = 0; i < 16; ++i) __asm__ volatile("v_mov_b32 %0, %1" : "+v"(negm[i]) : "v"(nm));
+#pragma unroll
+            for (int k = 0; k < KB; ++k)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) sb[nxt(k)][i] -= delta;
         }
     };
 
+    // S(0) sits in blocks 0 .. KB-1, the "current" blocks of step 0.
     for (int t = 0; t < nt; t += 3) {
-        step(std::integral_constant<int, 0>{}, s0, s1, s2, s0, t);
+        step(std::integral_constant<int, 0>{}, t);
         if (t + 1 >= nt) break;
-        step(std::integral_constant<int, 1>{}, s2, s0, s1, s2, t + 1);
+        step(std::integral_constant<int, 1>{}, t + 1);
         if (t + 2 >= nt) break;
-        step(std::integral_constant<int, 2>{}, s1, s2, s0, s1, t + 2);
+        step(std::integral_constant<int, 2>{}, t + 2);
     }
     __builtin_amdgcn_s_waitcnt(0x0070);   // no DMA may land after the workgroup's LDS is released
 
@@ -1066,8 +688,7 @@ void fa_fwd_f32_kernel(FaArgs a) {
 
 // Query rows one workgroup covers (the host sizes the grid with it).
 int flash_attn_rows_per_workgroup(bool bf16, int64_t head_dim) {
-    if (bf16 && head_dim == 128) return 32 * FAD_WAVES;
-    return bf16 ? 32 * FA_QG * FA_WAVES : 256 / (int)(head_dim / 32);
+    return bf16 ? 32 * FAD_WAVES : 256 / (int)(head_dim / 32);
 }
 
 hipError_t launch_flash_attn(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -1103,16 +724,15 @@ hipError_t launch_flash_attn(const void* q, const void* k, const void* v, void* 
     a.total_tiles = batch * heads * a.n_qtiles;
     const dim3 grid((unsigned)a.total_tiles);
     if (bf16) {
-        const dim3 block(64 * FA_WAVES);
-        const dim3 dblock(64 * FAD_WAVES);
+        const dim3 block(64 * FAD_WAVES);
         if (head_dim == 128 && a.has_pad)
-            hipLaunchKernelGGL(fa_fwd_bf16_dma_kernel<true>, grid, dblock, 0, st, a);
+            hipLaunchKernelGGL((fa_fwd_bf16_dma_kernel<128, true>), grid, block, 0, st, a);
         else if (head_dim == 128)
-            hipLaunchKernelGGL(fa_fwd_bf16_dma_kernel<false>, grid, dblock, 0, st, a);
+            hipLaunchKernelGGL((fa_fwd_bf16_dma_kernel<128, false>), grid, block, 0, st, a);
         else if (a.has_pad)
-            hipLaunchKernelGGL((fa_fwd_bf16_kernel<64, FA_WAVES, FA_QG, true>), grid, block, 0, st, a);
+            hipLaunchKernelGGL((fa_fwd_bf16_dma_kernel<64, true>), grid, block, 0, st, a);
         else
-            hipLaunchKernelGGL((fa_fwd_bf16_kernel<64, FA_WAVES, FA_QG, false>), grid, block, 0, st, a);
+            hipLaunchKernelGGL((fa_fwd_bf16_dma_kernel<64, false>), grid, block, 0, st, a);
     } else {
         const dim3 block(256);
         if (head_dim == 128) hipLaunchKernelGGL(fa_fwd_f32_kernel<128>, grid, block, 0, st, a);

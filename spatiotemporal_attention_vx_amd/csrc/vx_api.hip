@@ -180,6 +180,8 @@ int flash_attn(const char* fn, const void* q, const void* k, const void* v, void
         return fail(VX_ERR_INVALID, "%s: softmax_scale must be finite", fn);
     if (head_dim != 64 && head_dim != 128)
         return fail(VX_ERR_UNSUPPORTED, "%s: head_dim %lld (64 or 128 only)", fn, (long long)head_dim);
+    if (nq > INT32_MAX || nk > INT32_MAX)
+        return fail(VX_ERR_UNSUPPORTED, "%s: token counts above 2^31 - 1", fn);
     vx::RopeArgs r;
     if (rope_q)
         if (int e = check_rope(fn, rope_q, nq, head_dim, &r)) return e;
