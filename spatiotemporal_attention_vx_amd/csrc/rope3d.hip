@@ -12,10 +12,12 @@
 // and by Q and K, so they cost one evaluation per token and pair), then
 // streams the 16-byte chunks of the tokens' Q and K rows, consecutive lanes
 // on consecutive chunks.  With adjacent pairs (pairing 0) both elements of
-// a pair sit in one chunk.  With the half-split pairings (1: halves of the
-// head, 2: halves of each band) a pair spans chunks, so each head row is
-// staged through LDS first and every lane reads its elements' partners
-// there.
+// a pair sit in one chunk.  With halves of the head (pairing 1) the two
+// elements sit in chunks c and c + (chunks per row) / 2 whenever head_dim / 2
+// is a whole number of chunks, and one thread rotates that chunk pair.
+// Otherwise (halves of each band, pairing 2, or an odd split) a pair spans
+// chunks irregularly, so each head row is staged through LDS first and every
+// lane reads its elements' partners there.
 #include "vx_device.h"
 
 namespace vx {
@@ -191,10 +193,75 @@ void rope3d_split_kernel(uint4* q, uint4* k, int64_t rows, int64_t n_tokens, int
     }
 }
 
+// Halves of the head (pairing 1) when head_dim / 2 is a whole number of
+// 16-byte chunks: element m of chunk c (c < half the row's chunks) pairs with
+// element m of chunk c + dpr / 2, so a thread loads both chunks and rotates
+// in registers, with the angle of pair c * EPC + m.
+template <bool BF16>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256)))
+void rope3d_halves_kernel(uint4* q, uint4* k, int64_t rows, int64_t n_tokens, int heads,
+                          int head_dim, RopeArgs r) {
+    constexpr int EPC = BF16 ? 8 : 4;
+    __shared__ f32x2_t cs[ROPE_TPB * ROPE_MAX_HALF];
+    __shared__ int rotate[ROPE_TPB];
+    const int half = head_dim >> 1;
+    const int64_t row0 = (int64_t)blockIdx.x * ROPE_TPB;
+    for (int i = threadIdx.x; i < ROPE_TPB * half; i += 256) {
+        const int tk = i / half, pair = i - tk * half;
+        const int64_t row = row0 + tk;
+        float c = 1.f, s = 0.f;
+        int tp, hp, wp;
+        if (row < rows && rope_token_pos(r, row % n_tokens, &tp, &hp, &wp))
+            rope_cos_sin(r, rope_pair_pos(r, pair, tp, hp, wp), pair, &c, &s);
+        cs[i] = f32x2_t{c, s};
+    }
+    if (threadIdx.x < ROPE_TPB) {
+        const int64_t row = row0 + threadIdx.x;
+        rotate[threadIdx.x] = row < rows && (row % n_tokens) >= r.n_prefix;
+    }
+    __syncthreads();
+
+    const int dpr = head_dim / EPC, hc = dpr / 2;   // chunks per head row, and per half
+    const int per_token = heads * hc;                // chunk pairs per token row
+    // walk (token, tensor, head, chunk pair) with the chunk pair fastest
+    for (int u = threadIdx.x; u < ROPE_TPB * 2 * per_token; u += 256) {
+        const int tw = u / per_token, rem = u - tw * per_token;
+        const int which = tw & 1, tk = tw >> 1;
+        const int h = rem / hc, c = rem - h * hc;
+        uint4* base = which ? k : q;
+        if (base == nullptr || !rotate[tk]) continue;
+        uint4* p0 = base + ((row0 + tk) * heads + h) * dpr + c;
+        uint4* p1 = p0 + hc;
+        const uint4 v0 = *p0, v1 = *p1;
+        float f0[EPC], f1[EPC];
+        unpack_chunk<BF16>(u32x4_t{v0.x, v0.y, v0.z, v0.w}, f0);
+        unpack_chunk<BF16>(u32x4_t{v1.x, v1.y, v1.z, v1.w}, f1);
+        const f32x2_t* t = cs + tk * half + c * EPC;
+#pragma unroll
+        for (int m = 0; m < EPC; ++m) {
+            const f32x2_t e = t[m];
+            rope_rotate(f0[m], f1[m], e.x, e.y);
+        }
+        const u32x4_t w0 = pack_chunk<BF16>(f0), w1 = pack_chunk<BF16>(f1);
+        *p0 = uint4{w0[0], w0[1], w0[2], w0[3]};
+        *p1 = uint4{w1[0], w1[1], w1[2], w1[3]};
+    }
+}
+
 hipError_t launch_rope3d(void* q, void* k, int64_t batch, int64_t n_tokens, int64_t heads,
                          int64_t head_dim, const RopeArgs& r, bool bf16, hipStream_t st) {
     const int64_t rows = batch * n_tokens;
     const int64_t blocks = (rows + ROPE_TPB - 1) / ROPE_TPB;
+    const int epc = bf16 ? 8 : 4;
+    if (r.pairing == 1 && (head_dim / 2) % epc == 0) {
+        if (bf16)
+            hipLaunchKernelGGL(rope3d_halves_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, st,
+                               (uint4*)q, (uint4*)k, rows, n_tokens, (int)heads, (int)head_dim, r);
+        else
+            hipLaunchKernelGGL(rope3d_halves_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, st,
+                               (uint4*)q, (uint4*)k, rows, n_tokens, (int)heads, (int)head_dim, r);
+        return hipGetLastError();
+    }
     if (r.pairing != 0) {
         if (bf16)
             hipLaunchKernelGGL(rope3d_split_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, st,
