@@ -217,6 +217,29 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
+    # AdaLN and RoPE alone, 100 back-to-back launches each after 3 warm-ups,
+    # each launch bracketed by HIP events on the same stream (RoPE rotates K
+    # again on every launch: harmless for timing)
+    def reps(fn, n=100):
+        for _ in range(3):
+            fn()
+        pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                 for _ in range(n)]
+        for a_, b_ in pairs:
+            a_.record(stream)
+            fn()
+            b_.record(stream)
+        torch.cuda.synchronize()
+        t = np.array([a_.elapsed_time(b_) for a_, b_ in pairs])
+        return {"reps": n, "median_ms": round(float(np.median(t)), 4),
+                "mean_ms": round(float(t.mean()), 4)}
+
+    adaln_call = ((lambda: binding.adaln_modulate(tx, tsh, tsc, ty, wl.eps, stream=stream))
+                  if args.adaln == "token" else
+                  (lambda: binding.adaln_modulate_ex(tx, tsh, tsc, ty, wl.eps, stream=stream)))
+    rep_adaln = reps(adaln_call)
+    rep_rope = reps(lambda: binding.rope3d_apply(None if fused else tq, tk, desc, stream=stream))
+
     if args.copy_calibration:
         src = torch.empty(1 << 29, dtype=torch.bfloat16, device=dev).normal_()
         dst = torch.empty_like(src)
@@ -231,8 +254,10 @@ def main():
     value = flops / (ms_step * 1e-3) / 1e12
     attn_tflops = flops / (ms["attn"] * 1e-3) / 1e12
     rope_bytes = wl.rope_bytes() / (1 if not fused else 2)     # fused: K only
+    attn_all = [a_.elapsed_time(b_) for a_, b_ in ev["attn"]]
     kernels = {
         "attn_ms": round(ms["attn"], 4),
+        "attn_ms_median": round(float(np.median(attn_all)), 4),
         "attn_tflops": round(attn_tflops, 2),
         "attn_exps": float(wl.n_tokens) ** 2 * wl.heads,
         "adaln_ms": round(ms["adaln"], 4),
@@ -245,6 +270,10 @@ def main():
         "rope_gbs": round(rope_bytes / (ms["rope"] * 1e-3) / 1e9, 1),
         "rope_hbm_frac": round(rope_bytes / (ms["rope"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
     }
+    kernels["adaln_100"] = dict(rep_adaln, hbm_frac=round(
+        adaln_bytes / (rep_adaln["median_ms"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4))
+    kernels["rope_100"] = dict(rep_rope, hbm_frac=round(
+        rope_bytes / (rep_rope["median_ms"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4))
     if split:
         # o_a, o_b and both LSEs read, o written
         o_bytes = to.numel() * to.element_size()
