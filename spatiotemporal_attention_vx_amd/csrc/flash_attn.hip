@@ -38,7 +38,9 @@
 //       Y: O += V(t)^T P(t)   (MFMA)  interleaved with  row sum of P(t),
 //          row max of S(t+1)
 //     with the tile loads for later iterations spread over both phases and
-//     one barrier per tile.  Each MFMA and the work meant to run under it
+//     one barrier per tile, halfway through Y: the waves pass it with the
+//     rest of Y's MFMAs still to issue, which covers the LDS reads of the
+//     next tile's first K fragments.  Each MFMA and the work meant to run under it
 //     form a group that sched_barrier(0) keeps in order.
 //   * Tiles past the sequence end are read through a buffer resource that
 //     ends at the sequence end, so they load as zeros with no per-lane test;
@@ -448,7 +450,8 @@ void fa_fwd_bf16_dma_kernel(FaArgs a) {
 
     // Step t uses K buffers (t+1) % 3 (read), (t+2) % 3 (next tile's first
     // fragments), t % 3 (DMA target) and V buffers t % 3 (read), (t+2) % 3
-    // (DMA target); the loop is unrolled three times so all are compile-time.
+    // (DMA target, refilled after the step's barrier); the loop is unrolled
+    // three times so all are compile-time.
     auto step = [&](auto tm, int t) {
         constexpr int J = decltype(tm)::value;   // t % 3
         constexpr int NX = KB * NKK;          // K fragments (MFMAs) of S(t+1)
@@ -492,10 +495,28 @@ void fa_fwd_bf16_dma_kernel(FaArgs a) {
         float mx = -__builtin_inff(), psum = l_run;
 #pragma unroll
         for (int i = 0; i < NY; ++i) {
+            if (i == NY / 2) {
+                // Mid-step barrier.  Before it each wave waits for its own
+                // share of K(t+2) and V(t+1) (the K(t+3) requests issued in
+                // X may stay in flight; vmcnt counts only the tile DMAs);
+                // after it those tiles are whole in LDS, and every wave is
+                // done with K(t+1) and V(t-1), whose buffers may be refilled.
+                // The first K(t+2) fragments are read here, so the next
+                // step's first MFMA does not wait on LDS.  No fence: only the
+                // DMAs need ordering, and the explicit wait covers them.
+                __builtin_amdgcn_s_waitcnt(0x0F70 | NI);
+                __asm__ volatile("" ::: "memory");
+                __builtin_amdgcn_s_barrier();
+                __asm__ volatile("" ::: "memory");
+                kf[0] = kfrag(j2, 0);
+                kf[1] = kfrag(j2, 1);
+            }
             if (i + 2 < NY) vf[(i + 2) % 3] = vfrag(j0, i + 2);
             acc[i / KS] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i % 3], pb[i % KS], acc[i / KS], 0, 0, 0);
-            // V(t+2) where V(t-1) was, one request every NY / NI groups
-            if (i % (NY / NI) == 0) dma_one(vb, tl.at(t + 2), vbuf(j2), i / (NY / NI));
+            // V(t+2) where V(t-1) was, after the barrier, one request every
+            // NY / 2 / NI groups
+            if (i >= NY / 2 && (i - NY / 2) % (NY / 2 / NI) == 0)
+                dma_one(vb, tl.at(t + 2), vbuf(j2), (i - NY / 2) / (NY / 2 / NI));
             if (i < NY / 2) {
 #pragma unroll
                 for (int e = 0; e < SPM; ++e)
@@ -513,13 +534,6 @@ void fa_fwd_bf16_dma_kernel(FaArgs a) {
         }
         l_run = psum;
         mx_next = half_max(mx);
-        // The tiles DMA'd in the previous iteration (K(t+2), V(t+1)) are
-        // read after this barrier; this iteration's 2 NI requests may stay
-        // in flight.  vmcnt counts only these DMAs in the loop.
-        __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * NI));
-        __syncthreads();
-        kf[0] = kfrag(j2, 0);
-        kf[1] = kfrag(j2, 1);
         // ---- keys past the end or padded take no weight
         if (t + 1 < nt && tl.masked(tl.at(t + 1))) {
             mask_tile(tm, tl.at(t + 1));
