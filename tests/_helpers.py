@@ -65,3 +65,33 @@ def check(got, ref, dtype, what=""):
         assert max_abs <= BF16_MAX_ABS, f"{what}: max abs {max_abs:.3e} > {BF16_MAX_ABS}"
         assert rel <= BF16_REL_L2, f"{what}: rel L2 {rel:.3e} > {BF16_REL_L2}"
     return max_abs, rel
+
+
+class ChunkCheck:
+    """The tolerance check over a tensor compared chunk by chunk: max abs over
+    all chunks, relative L2 from the summed squares of every chunk."""
+
+    def __init__(self, dtype, what):
+        self.dtype, self.what = dtype, what
+        self.max_abs, self.d2, self.r2, self.n = 0.0, 0.0, 0.0, 0
+
+    def add(self, got, ref):
+        got = np.asarray(got, dtype=np.float64)
+        ref = np.asarray(ref, dtype=np.float64)
+        assert np.all(np.isfinite(got)), f"{self.what}: non-finite output"
+        d = got - ref
+        if d.size:
+            self.max_abs = max(self.max_abs, float(np.abs(d).max()))
+        self.d2 += float(np.sum(d * d))
+        self.r2 += float(np.sum(ref * ref))
+        self.n += d.size
+
+    def done(self):
+        rel = float(np.sqrt(self.d2 / self.r2)) if self.r2 > 0 else float(np.sqrt(self.d2))
+        say(f"  {self.what}: {self.n} values, max_abs={self.max_abs:.3e} rel_l2={rel:.3e}")
+        if self.dtype == "f32":
+            assert self.max_abs <= F32_MAX_ABS, f"{self.what}: max abs {self.max_abs:.3e}"
+        else:
+            assert self.max_abs <= BF16_MAX_ABS, f"{self.what}: max abs {self.max_abs:.3e}"
+            assert rel <= BF16_REL_L2, f"{self.what}: rel L2 {rel:.3e}"
+        return self.max_abs, rel
