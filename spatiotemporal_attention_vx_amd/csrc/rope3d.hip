@@ -90,15 +90,25 @@ void rope3d_kernel(uint4* q, uint4* k, int64_t rows, int64_t n_tokens, int heads
     }
 }
 
-// Half-split pairings.  Each wave works through its own share of the
-// workgroup's (token, tensor, head) rows, 64 / (head_dim / EPC) rows per
-// pass and ROPE_SPLIT_U passes at once: every lane loads one 16-byte chunk
-// of each of its U rows (U loads in flight), keeps the values and writes
-// them to the wave's own LDS area; the wave then rotates every element with
-// its partner read from LDS and stores the chunks back.  Only lanes of one
-// wave share an LDS area, so a wave-level barrier orders the writes and the
-// reads; waves never wait for each other inside the loop.
+// Half-split pairings (halves of each band, or halves of the head when a
+// half is not a whole number of chunks).  One wave owns one token: every
+// (tensor, head) row of it in Q and K.  The wave first evaluates its token's
+// cos/sin for all head_dim/2 pairs into its own LDS area, and each lane keeps
+// those of its chunk's elements in registers for every row.  Rows then go
+// 64 / (head_dim / EPC) per pass and ROPE_SPLIT_U passes at once: every lane
+// loads one 16-byte chunk of each of its U rows (U loads in flight), stages
+// the raw chunk in the wave's LDS area, and after a wave-level barrier
+// rotates each element with its partner read back from there and stores the
+// chunk.  A staged row is padded by one 32-bit word, so the rows of a pass
+// start on different banks: the partner reads of a wave then hit each bank
+// at most twice for the band splits in use, and the chunk writes never
+// conflict.  Only lanes of one wave share an LDS area, so waves never wait
+// for each other.  Two passes per batch keep the workgroup's LDS at 14 KiB,
+// so eight workgroups (32 waves) fit a CU: more passes per batch cost
+// occupancy and measured slower.
 constexpr int ROPE_SPLIT_U = 2;
+// staging words per pass and wave: rows x (row + 1 padding word) <= 256 + 64
+constexpr int ROPE_SPLIT_WORDS = 320;
 
 __device__ __forceinline__ void wave_sync_lds() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -110,81 +120,79 @@ template <bool BF16>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256)))
 void rope3d_split_kernel(uint4* q, uint4* k, int64_t rows, int64_t n_tokens, int heads,
                          int head_dim, RopeArgs r) {
+    static_assert(ROPE_TPB == 4, "one wave per token of the workgroup");
     constexpr int EPC = BF16 ? 8 : 4;
     constexpr int U = ROPE_SPLIT_U;
-    __shared__ f32x2_t cs[ROPE_TPB * ROPE_MAX_HALF];
-    __shared__ float xs[4][U * 64 * EPC];   // per wave: U passes x 64 lanes x EPC values
-    __shared__ int rotate[ROPE_TPB];        // token exists and is not text
-    const int half = head_dim >> 1;
-    const int64_t row0 = (int64_t)blockIdx.x * ROPE_TPB;
-
-    for (int i = threadIdx.x; i < ROPE_TPB * half; i += 256) {
-        const int tk = i / half, pair = i - tk * half;
-        const int64_t row = row0 + tk;
-        float c = 1.f, s = 0.f;
-        int tp, hp, wp;
-        if (row < rows && rope_token_pos(r, row % n_tokens, &tp, &hp, &wp))
-            rope_cos_sin(r, rope_pair_pos(r, pair, tp, hp, wp), pair, &c, &s);
-        cs[i] = f32x2_t{c, s};
-    }
-    if (threadIdx.x < ROPE_TPB) {
-        const int64_t row = row0 + threadIdx.x;
-        rotate[threadIdx.x] = row < rows && (row % n_tokens) >= r.n_prefix;
-    }
-    __syncthreads();
-
+    __shared__ f32x2_t cs_all[4][ROPE_MAX_HALF];
+    __shared__ uint32_t stage_all[4][U * ROPE_SPLIT_WORDS];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * ROPE_TPB + wave;   // this wave's token row
+    if (row >= rows) return;
+    int tp, hp, wp;
+    if (!rope_token_pos(r, row % n_tokens, &tp, &hp, &wp)) return;   // text: not rotated
+    const int half = head_dim >> 1;
+    f32x2_t* const cs = cs_all[wave];
+    for (int j = lane; j < half; j += 64) {
+        float c, s;
+        rope_cos_sin(r, rope_pair_pos(r, j, tp, hp, wp), j, &c, &s);
+        cs[j] = f32x2_t{c, s};
+    }
     const int dpr = head_dim / EPC;            // chunks per head row (<= 32)
     const int rpp = 64 / dpr;                  // head rows per pass
     const int slot = lane / dpr, c = lane - slot * dpr;
-    // a lane always holds the same columns: their pairs are fixed
-    int pair[EPC], partner[EPC];
+    // staged row stride in 32-bit words: the row plus one word of padding
+    const int rs = (BF16 ? head_dim / 2 : head_dim) + 1;
+    int partner[EPC];
+    float cr[EPC], sr[EPC];
     uint32_t second = 0;
+    wave_sync_lds();
 #pragma unroll
     for (int m = 0; m < EPC; ++m) {
+        int pair;
         bool sec;
-        rope_elem_pair(r, c * EPC + m, &pair[m], &partner[m], &sec);
+        rope_elem_pair(r, c * EPC + m, &pair, &partner[m], &sec);
         second |= (uint32_t)sec << m;
+        const f32x2_t e = cs[pair];
+        cr[m] = e.x;
+        sr[m] = e.y;
     }
-    const int64_t units = (int64_t)ROPE_TPB * 2 * heads;   // (token, tensor, head), head fastest
-    float* const area = xs[wave];
-    // passes p = 0, 1, ... cover units p * rpp .. p * rpp + rpp - 1; wave w
-    // takes passes w * U .. w * U + U - 1, then 4 U further on, and so on
-    for (int64_t p0 = wave * U; p0 * rpp < units; p0 += 4 * U) {
-        float f[U][EPC];
+    uint32_t* const stage = stage_all[wave];
+    // rows of this token: Q heads 0..H-1, then K heads 0..H-1 (absent tensors skipped)
+    const int u_begin = q != nullptr ? 0 : heads, u_end = k != nullptr ? 2 * heads : heads;
+    const int64_t dpt = (int64_t)heads * dpr;   // chunks per token row
+    for (int u0 = u_begin; u0 < u_end; u0 += U * rpp) {
+        uint4 raw[U];
         uint4* ptr[U];
-        int tku[U];
 #pragma unroll
         for (int i = 0; i < U; ++i) {
-            const int64_t u = (p0 + i) * rpp + slot;
-            bool live = slot < rpp && u < units;
-            const int h = live ? (int)(u % heads) : 0, tw = live ? (int)(u / heads) : 0;
-            const int which = tw & 1, tk = tw >> 1;
-            uint4* base = which ? k : q;
-            live = live && base != nullptr && rotate[tk];
-            tku[i] = tk;
-            ptr[i] = live ? base + ((row0 + tk) * heads + h) * dpr + c : nullptr;
-            if (live) {
-                const uint4 v = *ptr[i];
-                unpack_chunk<BF16>(u32x4_t{v.x, v.y, v.z, v.w}, f[i]);
-            }
+            const int u = u0 + i * rpp + slot;
+            const bool live = slot < rpp && u < u_end;
+            uint4* base = u < heads ? q : k;
+            const int h = u < heads ? u : u - heads;
+            ptr[i] = live ? base + row * dpt + (int64_t)h * dpr + c : nullptr;
+            if (live) raw[i] = *ptr[i];
         }
 #pragma unroll
         for (int i = 0; i < U; ++i)
-            if (ptr[i] != nullptr)
-#pragma unroll
-                for (int m = 0; m < EPC; ++m) area[(i * rpp + slot) * head_dim + c * EPC + m] = f[i][m];
+            if (ptr[i] != nullptr) {
+                uint32_t* dst = stage + (i * rpp + slot) * rs + c * 4;
+                dst[0] = raw[i].x; dst[1] = raw[i].y; dst[2] = raw[i].z; dst[3] = raw[i].w;
+            }
         wave_sync_lds();
 #pragma unroll
         for (int i = 0; i < U; ++i) {
             if (ptr[i] == nullptr) continue;
-            const float* row = area + (i * rpp + slot) * head_dim;
-            const f32x2_t* cst = cs + tku[i] * half;
-            float out[EPC];
+            const uint32_t* srow = stage + (i * rpp + slot) * rs;
+            float f[EPC], out[EPC];
+            unpack_chunk<BF16>(u32x4_t{raw[i].x, raw[i].y, raw[i].z, raw[i].w}, f);
 #pragma unroll
             for (int m = 0; m < EPC; ++m) {
-                const f32x2_t e = cst[pair[m]];
-                out[m] = rope_rotate_elem(f[i][m], row[partner[m]], (second >> m) & 1, e.x, e.y);
+                float xp;
+                if constexpr (BF16)
+                    xp = __uint_as_float((uint32_t)((const uint16_t*)srow)[partner[m]] << 16);
+                else
+                    xp = __uint_as_float(srow[partner[m]]);
+                out[m] = rope_rotate_elem(f[m], xp, (second >> m) & 1, cr[m], sr[m]);
             }
             const u32x4_t w = pack_chunk<BF16>(out);
             *ptr[i] = uint4{w[0], w[1], w[2], w[3]};
