@@ -81,7 +81,10 @@ int check_rope(const char* fn, const vx_rope3d_desc* r, int64_t n_tokens, int64_
     if (r->T < 0 || r->H < 0 || r->W < 0 || r->n_prefix < 0)
         return fail(VX_ERR_INVALID, "%s: rope grid (%d,%d,%d) and prefix %d must be non-negative",
                     fn, r->T, r->H, r->W, r->n_prefix);
-    const int64_t nv = (int64_t)r->T * r->H * r->W;
+    int64_t nv;
+    if (!mul_ok(nv, {r->T, r->H, r->W}) || nv > INT64_MAX - r->n_prefix)
+        return fail(VX_ERR_INVALID, "%s: rope grid %dx%dx%d + prefix %d overflows", fn, r->T, r->H,
+                    r->W, r->n_prefix);
     if (nv + r->n_prefix != n_tokens)
         return fail(VX_ERR_INVALID, "%s: rope grid %dx%dx%d + prefix %d = %lld tokens, but n_tokens = %lld",
                     fn, r->T, r->H, r->W, r->n_prefix, (long long)(nv + r->n_prefix), (long long)n_tokens);

@@ -141,6 +141,7 @@ def test_adaln_zero_rows_is_a_no_op():
     (A, A + MB, 24, 64, _rope(pairing=3), INVALID),
     (A, A + MB, 24, 64, _rope(pairing=-1), INVALID),
     (A, A + MB, 24, 64, _rope(T=-1), INVALID),
+    (A, A + MB, 24, 64, _rope(T=2**30, H=2**30, W=2**30), INVALID),   # grid product overflows
     (A, A + MB, 24, 60, _rope(d_t=12), UNSUPPORTED),
     (A, A + MB, 24, 264, _rope(d_t=216), UNSUPPORTED),
     (A + 8, A + MB, 24, 64, _rope(), ALIGN),
