@@ -157,6 +157,11 @@ int vx_rope3d_apply(void* q, void* k, int64_t batch, int64_t n_tokens, int64_t h
  * registers as it is loaded (its buffer is not modified; the result equals
  * vx_rope3d_apply on Q first); K must already be rotated.  o must not
  * overlap q, k or v.
+ * Precision (bf16): scores and sums are fp32, P is rounded to bf16 for the
+ * P V product, and q * scale * log2(e) is rounded to bf16 once as Q is
+ * loaded.  The LSE therefore moves by up to about 2^-9 of the largest
+ * scale * sum_e |q_e k_e| of the row (0.07 at scores near 80); o is not
+ * affected beyond its bf16 tolerance, since softmax ignores a common shift.
  * Errors: VX_ERR_NULL (q, k, v or o NULL); VX_ERR_INVALID (sizes <= 0,
  * softmax_scale not finite, bad rope_q as for vx_rope3d_apply, o aliasing an
  * input); VX_ERR_UNSUPPORTED (head_dim not 64 or 128); VX_ERR_ALIGN.

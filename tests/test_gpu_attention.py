@@ -181,3 +181,55 @@ def test_mid_every_row(gpu_lib):
     acc.done()
     say(f"  lse max abs {lse_err:.3e}")
     assert lse_err <= LSE_TOL_ROPE[wl.dtype]
+
+
+def _aligned_scores(n, heads, d, pattern, seed):
+    """Q and K rows close to one unit direction per head, so scores reach
+    about 50-80 (natural units).  'rising': scores grow linearly along the
+    keys, so the kernel raises its running maximum again and again (about
+    every two key tiles).  'jump': the first half of the keys score near 0
+    and the second half near the top, so the maximum is raised once, by a
+    weight factor far below the float range."""
+    g = np.random.default_rng(seed)
+    q = np.empty((1, n, heads, d), np.float32)
+    k = np.empty((1, n, heads, d), np.float32)
+    v = g.standard_normal((1, n, heads, d)).astype(np.float32)
+    for h in range(heads):
+        u = g.standard_normal(d)
+        u /= np.linalg.norm(u)
+        a = 4.0 + 2.0 * g.random(n)
+        if pattern == "rising":
+            b = 12.0 * np.sqrt(d) * np.arange(n) / n
+        else:
+            b = np.where(np.arange(n) < n // 2, 0.0, 12.0 * np.sqrt(d))
+        q[0, :, h] = a[:, None] * u + 0.05 * g.standard_normal((n, d))
+        k[0, :, h] = b[:, None] * u + 0.05 * g.standard_normal((n, d))
+    return (inputs.storage(x, "bf16") for x in (q, k, v))
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("pattern", ["rising", "jump"])
+def test_large_rising_scores(gpu_lib, d, pattern):
+    """The lazy rescale under scores of 50-80: O to the usual bf16 tolerance.
+
+    The LSE bound follows from the kernel's one extra rounding.  It rounds
+    q * scale * log2(e) to bf16 (relative error at most 2^-9 per element), so
+    each score moves by at most 2^-9 * scale * sum_e |q_e k_e|.  The LSE, to
+    first order a softmax-weighted mean of the scores' moves, moves by at most
+    the largest of them.  The bf16 rounding of P adds at most 2^-9 (within
+    the 1e-2 floor).  The test allows twice that."""
+    n, heads = 1500, 2
+    say(f"attn large scores {pattern} d={d}")
+    q, k, v = _aligned_scores(n, heads, d, pattern, 11 + d)
+    o, lse = _attn(q, k, v)
+    qv, kv, vv = (inputs.values(x[0]).astype(np.float64) for x in (q, k, v))
+    ref, rl = oracle.attention(qv, kv, vv)
+    check(host(o)[0], ref, "bf16", f"o {pattern}")
+    scale = 1.0 / np.sqrt(d)
+    err = np.abs(lse.cpu().numpy()[0] - rl)
+    for h in range(heads):
+        moves = 2.0 ** -9 * scale * (np.abs(qv[:, h]) @ np.abs(kv[:, h]).T).max(axis=1)
+        bound = 1e-2 + 2.0 * moves
+        say(f"  head {h}: lse max abs {err[h].max():.3e}, largest score move bound "
+            f"{moves.max():.3e}, max lse {rl[h].max():.1f}")
+        assert np.all(err[h] <= bound)
