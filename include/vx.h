@@ -164,7 +164,8 @@ int vx_rope3d_apply(void* q, void* k, int64_t batch, int64_t n_tokens, int64_t h
  * affected beyond its bf16 tolerance, since softmax ignores a common shift.
  * Errors: VX_ERR_NULL (q, k, v or o NULL); VX_ERR_INVALID (sizes <= 0,
  * softmax_scale not finite, bad rope_q as for vx_rope3d_apply, o aliasing an
- * input); VX_ERR_UNSUPPORTED (head_dim not 64 or 128); VX_ERR_ALIGN.
+ * input); VX_ERR_UNSUPPORTED (head_dim not 64 or 128, more than 2^30 tokens, or
+ * heads * head_dim above 2^22); VX_ERR_ALIGN.
  */
 int vx_flash_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                       int64_t batch, int64_t n_tokens, int64_t heads, int64_t head_dim,

@@ -77,6 +77,8 @@ struct FaArgs {
     int64_t batch_stride;     // elements between batch entries of q and o (nq * heads * D)
     int64_t kv_batch_stride;  // elements between batch entries of k and v (nk * heads * D)
     int heads;
+    int dma_row_bytes;        // bytes per K/V token row (bf16), below 2^31
+    int dma_max_rows;         // rows whose bytes fit a buffer resource (2^31 - 1); >= 128
     int n_qtiles;
     int64_t total_tiles;
     float scale;           // softmax scale (natural units)
@@ -335,9 +337,16 @@ void fa_fwd_bf16_dma_kernel(FaArgs a) {
     // every DMA in flight (vmcnt(0)) before each V read.  Ordering is kept by
     // hand instead: an explicit vmcnt wait and the barrier publish a tile,
     // and no buffer is a DMA target while any wave may still read it.
+    // The resource's size is clamped in 32-bit scalar arithmetic, branch-free
+    // (token counts are below 2^30, so kv0 fits; int64 compares would go to
+    // the VALU).  dma_max_rows >= 128 >= BC, so a clamped size still covers
+    // the whole tile.
     auto dma_one = [&](const uint16_t* base, int t, lds_u8* buf, int m) {
-        const int64_t kv0 = (int64_t)t * BC;
-        const __amdgpu_buffer_rsrc_t r = buffer_rsrc(base + kv0 * a.row_stride, (nk - kv0) * row_bytes);
+        const int kv0 = t * BC;
+        const int rows_left = __builtin_elementwise_min(__builtin_elementwise_max(tl.nk - kv0, 0), a.dma_max_rows);
+        const int bytes = rows_left * a.dma_row_bytes;
+        const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t*>(base + (int64_t)kv0 * a.row_stride), (short)0, bytes, 0x00020000);
         const uint32_t dst = (uint32_t)(uintptr_t)(buf + (swave * NI + m) * 1024);
         __asm__ volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                          :
@@ -727,6 +736,8 @@ hipError_t launch_flash_attn(const void* q, const void* k, const void* v, void* 
     a.batch_stride = nq * heads * head_dim;
     a.kv_batch_stride = nk * heads * head_dim;
     a.heads = (int)heads;
+    a.dma_row_bytes = (int)(heads * head_dim * 2);
+    a.dma_max_rows = 0x7fffffff / a.dma_row_bytes;
     a.scale = scale;
     a.scale_log2 = scale * 1.4426950408889634f;
     a.use_rope = rope != nullptr;

@@ -183,8 +183,12 @@ int flash_attn(const char* fn, const void* q, const void* k, const void* v, void
         return fail(VX_ERR_INVALID, "%s: softmax_scale must be finite", fn);
     if (head_dim != 64 && head_dim != 128)
         return fail(VX_ERR_UNSUPPORTED, "%s: head_dim %lld (64 or 128 only)", fn, (long long)head_dim);
-    if (nq > INT32_MAX || nk > INT32_MAX)
-        return fail(VX_ERR_UNSUPPORTED, "%s: token counts above 2^31 - 1", fn);
+    if (nq > (int64_t(1) << 30) || nk > (int64_t(1) << 30))
+        return fail(VX_ERR_UNSUPPORTED, "%s: token counts above 2^30", fn);
+    // a tile of up to 128 token rows must fit one 2^31-byte buffer resource
+    if (heads * head_dim > (int64_t(1) << 22))
+        return fail(VX_ERR_UNSUPPORTED, "%s: heads * head_dim %lld above 2^22", fn,
+                    (long long)(heads * head_dim));
     vx::RopeArgs r;
     if (rope_q)
         if (int e = check_rope(fn, rope_q, nq, head_dim, &r)) return e;

@@ -182,6 +182,8 @@ def test_attention_rejects(ptrs, n, d, scale, rope, dt, code):
     ((A, A + MB, A + 2 * MB, A + 3 * MB, None), 24, 30, 64, _rope(T=3), INVALID),  # grid != n_q
     ((A, A + MB, A + 2 * MB, A + MB + 64, None), 24, 30, 64, None, INVALID),     # o overlaps k
     ((A, A + MB, A + 2 * MB, A + 3 * MB + 8, None), 24, 30, 64, None, ALIGN),
+    ((A, A + MB, A + 2 * MB, A + 3 * MB, None), 2**30 + 1, 30, 64, None, UNSUPPORTED),
+    ((A, A + MB, A + 2 * MB, A + 3 * MB, None), 24, 2**30 + 1, 64, None, UNSUPPORTED),
 ])
 def test_attention_kv_rejects(ptrs, nq, nk, d, rope, code):
     lib = binding.load()
@@ -235,3 +237,13 @@ def test_binding_refuses_mismatched_tensors():
     x = torch.zeros(4, 64)
     with pytest.raises(ValueError):
         binding.adaln_modulate(x, x, x, x)          # not on a GPU
+
+
+@host_only
+def test_attention_rejects_rows_too_wide_for_one_buffer():
+    """heads * head_dim above 2^22: a 128-row key tile would pass 2^31 bytes."""
+    lib = binding.load()
+    heads = 2**22 // 64 + 1
+    assert lib.vx_flash_attn_fwd(A, A + MB, A + 2 * MB, A + 3 * MB, None, 1, 1, heads, 64, 0.0,
+                                 None, 1, None) == UNSUPPORTED
+    assert b"2^22" in lib.vx_last_error()
