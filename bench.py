@@ -62,6 +62,10 @@ def parse():
                         "LSEs (vx_flash_attn_fwd_kv twice + vx_attn_merge2); 0 = one call")
     p.add_argument("--cpu-rows", type=int, default=512,
                    help="query rows of the oracle CPU baseline (0 = skip it)")
+    p.add_argument("--inputs", choices=["normal", "zeros"], default="normal",
+                   help="normal: the workload's seeded N(0,1) tensors (the metric); zeros: "
+                        "every input set to zero on the GPU, a power diagnosis only (the "
+                        "kernels run the same instructions; the line is marked diagnostic)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run a plain 1 GiB elementwise copy (HBM counter calibration)")
     return p.parse_args()
@@ -81,7 +85,7 @@ def measured_traffic(wl, args, pairing):
     import hashlib
     path = os.path.join(ROOT, "profiles", "attention_large_traffic.json")
     if (wl.name != "large" or args.kv_split or args.rope != "fused" or pairing != 0
-            or not os.path.exists(path)):
+            or getattr(args, "inputs", "normal") != "normal" or not os.path.exists(path)):
         return None
     with open(path) as f:
         rec = json.load(f)
@@ -160,6 +164,9 @@ def main():
         ty = torch.empty(tx.shape, dtype=torch.bfloat16, device=dev)
     adaln_bytes = sum(t.numel() * t.element_size() for t in (tx, tsh, tsc, ty))
     to = torch.empty_like(tq)
+    if args.inputs == "zeros":
+        for t in (tq, tk, tv, tx, tsh, tsc):
+            t.zero_()
     gen_s = time.perf_counter() - t0
     pairing = wl.pairing if args.pairing is None else args.pairing
     desc = binding.RopeDesc.of(wl.grid, wl.split, wl.theta, wl.n_prefix, pairing)
@@ -331,7 +338,12 @@ def main():
                    "gcn_arch": getattr(props, "gcnArchName", "")},
         "input_setup_s": round(gen_s, 2),
     }
-    if args.cpu_rows > 0:
+    if args.inputs == "zeros":
+        record["data"] = "synthetic, every input zero"
+        record["diagnostic"] = ("all-zero inputs: the same launches and instructions with "
+                                "almost no data toggling, to separate the chip's power limit "
+                                "from the kernel's schedule; not the metric's workload")
+    if args.cpu_rows > 0 and args.inputs == "normal":
         record["cpu_baseline"] = cpu_baseline(wl, q, k, v, args.cpu_rows, pairing)
     print(json.dumps(record), flush=True)
 
