@@ -341,6 +341,11 @@ void fa_fwd_bf16_dma_kernel(FaArgs a) {
     // (token counts are below 2^30, so kv0 fits; int64 compares would go to
     // the VALU).  dma_max_rows >= 128 >= BC, so a clamped size still covers
     // the whole tile.
+    // M0 is a reserved register, so the compiler warns that listing it as
+    // clobbered does not make it save or restore it.  That is safe here only
+    // because nothing the compiler generates in these kernels reads or
+    // writes M0 (no LDS-direct, GWS, movrel or message instructions); the
+    // host test suite compiles this file and checks exactly that.
     auto dma_one = [&](const uint16_t* base, int t, lds_u8* buf, int m) {
         const int kv0 = t * BC;
         const int rows_left = __builtin_elementwise_min(__builtin_elementwise_max(tl.nk - kv0, 0), a.dma_max_rows);
