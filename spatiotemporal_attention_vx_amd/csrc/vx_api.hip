@@ -186,9 +186,10 @@ int flash_attn(const char* fn, const void* q, const void* k, const void* v, void
     if (nq > (int64_t(1) << 30) || nk > (int64_t(1) << 30))
         return fail(VX_ERR_UNSUPPORTED, "%s: token counts above 2^30", fn);
     // a tile of up to 128 token rows must fit one 2^31-byte buffer resource
-    if (heads * head_dim > (int64_t(1) << 22))
-        return fail(VX_ERR_UNSUPPORTED, "%s: heads * head_dim %lld above 2^22", fn,
-                    (long long)(heads * head_dim));
+    // (compared by division: heads * head_dim itself may not fit in int64)
+    if (heads > (int64_t(1) << 22) / head_dim)
+        return fail(VX_ERR_UNSUPPORTED, "%s: heads %lld * head_dim %lld above 2^22", fn,
+                    (long long)heads, (long long)head_dim);
     vx::RopeArgs r;
     if (rope_q)
         if (int e = check_rope(fn, rope_q, nq, head_dim, &r)) return e;

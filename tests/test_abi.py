@@ -247,3 +247,19 @@ def test_attention_rejects_rows_too_wide_for_one_buffer():
     assert lib.vx_flash_attn_fwd(A, A + MB, A + 2 * MB, A + 3 * MB, None, 1, 1, heads, 64, 0.0,
                                  None, 1, None) == UNSUPPORTED
     assert b"2^22" in lib.vx_last_error()
+
+
+@host_only
+def test_attention_rejects_head_counts_whose_width_overflows_int64():
+    """heads near 2^62: heads * head_dim would not fit in int64; rejected, not wrapped."""
+    lib = binding.load()
+    for heads in (2**62, 2**63 - 1):
+        assert lib.vx_flash_attn_fwd(A, A + MB, A + 2 * MB, A + 3 * MB, None, 1, 1, heads, 128,
+                                     0.0, None, 1, None) == UNSUPPORTED
+        assert b"2^22" in lib.vx_last_error()
+    # the largest width allowed passes this check, then stops at the overlap of the fake
+    # 1 MiB-apart pointers (8 MiB tensors), before any launch
+    heads = 2**22 // 128
+    assert lib.vx_flash_attn_fwd(A, A + MB, A + 2 * MB, A + 3 * MB, None, 1, 1, heads, 128,
+                                 0.0, None, 1, None) == INVALID
+    assert b"overlaps" in lib.vx_last_error()
