@@ -250,6 +250,12 @@ def main():
     rep_adaln = reps(adaln_call)
     rep_rope = reps(lambda: binding.rope3d_apply(None if fused else tq, tk, desc, stream=stream))
 
+    # The bf16 MFMA rate this chip sustains on the same kind of data: a pure
+    # v_mfma loop timed on this machine right after the step (its clock is set by
+    # the power limit, which depends on the operand data).
+    from spatiotemporal_attention_vx_amd import diag
+    ceiling = diag.ceiling("zeros" if args.inputs == "zeros" else "normal")
+
     if args.copy_calibration:
         src = torch.empty(1 << 29, dtype=torch.bfloat16, device=dev).normal_()
         dst = torch.empty_like(src)
@@ -332,6 +338,15 @@ def main():
             "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
             "traffic": measured_traffic(wl, args, pairing),
             "kernel": attention_kernel_name(wl),
+            "measured_ceiling": {
+                "tflops": round(ceiling["tflops"], 1),
+                "frac_of_peak": round(ceiling["tflops"] / PEAK_BF16_TFLOPS, 4),
+                "attn_frac_of_ceiling": round(attn_tflops / ceiling["tflops"], 4),
+                "what": ("pure v_mfma_f32_32x32x16_bf16 loop on "
+                         + ("all-zero" if args.inputs == "zeros" else "N(0,1) bf16")
+                         + f" operands, {ceiling['launch']}, same box, same run: the rate the "
+                           "chip's power limit allows on this data"),
+            },
         },
         "kernels": kernels,
         "device": {"name": props.name, "cus": props.multi_processor_count,
