@@ -249,6 +249,11 @@ def main():
                   (lambda: binding.adaln_modulate_ex(tx, tsh, tsc, ty, wl.eps, stream=stream)))
     rep_adaln = reps(adaln_call)
     rep_rope = reps(lambda: binding.rope3d_apply(None if fused else tq, tk, desc, stream=stream))
+    # Reference for AdaLN's access pattern on this machine: torch's own elementwise
+    # kernel streaming the same four tensors (three read, one written), timed
+    # the same way.  Not part of the step.
+    rep_stream = (reps(lambda: torch.addcmul(tsh, tx, tsc, out=ty))
+                  if args.adaln == "token" else None)
 
     # The bf16 MFMA rate this chip sustains on the same kind of data: a pure
     # v_mfma loop timed on this machine right after the step (its clock is set by
@@ -291,6 +296,12 @@ def main():
                            "their GB/s is cache bandwidth, not HBM")
     kernels["adaln_100"] = dict(rep_adaln, hbm_frac=round(
         adaln_bytes / (rep_adaln["median_ms"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4))
+    if rep_stream is not None:
+        kernels["adaln_pattern_reference"] = dict(
+            rep_stream, hbm_frac=round(
+                adaln_bytes / (rep_stream["median_ms"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            what="torch.addcmul over the same x, shift, scale and y (3 reads + 1 write, bf16), "
+                 "100 launches: plain elementwise streaming of AdaLN's bytes on this box")
     kernels["rope_100"] = dict(rep_rope, hbm_frac=round(
         rope_bytes / (rep_rope["median_ms"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4))
     if split:
