@@ -263,3 +263,30 @@ def test_attention_rejects_head_counts_whose_width_overflows_int64():
     assert lib.vx_flash_attn_fwd(A, A + MB, A + 2 * MB, A + 3 * MB, None, 1, 1, heads, 128,
                                  0.0, None, 1, None) == INVALID
     assert b"overlaps" in lib.vx_last_error()
+
+
+@host_only
+def test_error_string_is_per_thread():
+    """Eight threads fail calls concurrently (ctypes releases the GIL), each with
+    its own bad token count; each thread reads back its own message."""
+    import threading
+    lib = binding.load()
+    start = threading.Barrier(8)
+    bad = []
+
+    def worker(i):
+        start.wait()
+        for _ in range(300):
+            code = lib.vx_adaln_modulate(A, A + MB, A + 2 * MB, A + 3 * MB, -(i + 1), 64, 1e-6,
+                                         1, None)
+            msg = lib.vx_last_error().decode()
+            if code != INVALID or f"n_tokens {-(i + 1)}," not in msg:
+                bad.append((i, code, msg))
+                return
+
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(8)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not bad, bad[:3]
