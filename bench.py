@@ -254,6 +254,9 @@ def main():
     # the same way.  Not part of the step.
     rep_stream = (reps(lambda: torch.addcmul(tsh, tx, tsc, out=ty))
                   if args.adaln == "token" else None)
+    # and for RoPE's (K read and written in place; a multiply by one keeps the
+    # bits), when only K is rotated in the step
+    rep_rope_stream = reps(lambda: tk.mul_(1)) if fused else None
 
     # The bf16 MFMA rate this chip sustains on the same kind of data: a pure
     # v_mfma loop timed on this machine right after the step (its clock is set by
@@ -307,6 +310,12 @@ def main():
                 adaln_bytes / (rep_stream["median_ms"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
             what="torch.addcmul over the same x, shift, scale and y (3 reads + 1 write, bf16), "
                  "100 launches: plain elementwise streaming of AdaLN's bytes on this box")
+    if rep_rope_stream is not None:
+        kernels["rope_pattern_reference"] = dict(
+            rep_rope_stream, hbm_frac=round(
+                rope_bytes / (rep_rope_stream["median_ms"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            what="torch.mul_(1) on K in place (1 read + 1 write, bf16), 100 launches: plain "
+                 "elementwise streaming of RoPE's bytes on this box")
     kernels["rope_100"] = dict(rep_rope, hbm_frac=round(
         rope_bytes / (rep_rope["median_ms"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4))
     if split:

@@ -25,45 +25,63 @@ namespace vx {
 constexpr int ROPE_TPB = 4;          // tokens per workgroup
 constexpr int ROPE_MAX_HALF = ROPE_MAX_PAIRS;
 
+// Adjacent pairs.  Every thread owns the (token, tensor, chunk) items
+// threadIdx.x + 256 j of its workgroup, chunk index fastest, and handles
+// them ROPE_BATCH at a time: all loads of a batch are issued before any
+// chunk is rotated and stored, so each thread keeps ROPE_BATCH 16-byte loads
+// in flight (a load issued after a store to another chunk could not be moved
+// above it).  The first batch is loaded before the angles are evaluated, so
+// the sin/cos work runs under those loads.  Text-prefix rows are read but
+// never written.
+constexpr int ROPE_BATCH = 8;
+
 template <bool BF16>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256)))
 void rope3d_kernel(uint4* q, uint4* k, int64_t rows, int64_t n_tokens, int heads,
                    int head_dim, RopeArgs r) {
     constexpr int EPC = BF16 ? 8 : 4;    // elements per 16-byte chunk
     __shared__ f32x2_t cs[ROPE_TPB * ROPE_MAX_HALF];
+    __shared__ int rotate[ROPE_TPB];     // token exists and is not text
     const int half = head_dim >> 1;
     const int64_t row0 = (int64_t)blockIdx.x * ROPE_TPB;
-
-    for (int i = threadIdx.x; i < ROPE_TPB * half; i += 256) {
-        const int tk = i / half, pair = i - tk * half;
-        const int64_t row = row0 + tk;
-        float c = 1.f, s = 0.f;
-        int tp, hp, wp;
-        if (row < rows && rope_token_pos(r, row % n_tokens, &tp, &hp, &wp))
-            rope_cos_sin(r, rope_pair_pos(r, pair, tp, hp, wp), pair, &c, &s);
-        cs[i] = f32x2_t{c, s};
-    }
-    __shared__ int rotate[ROPE_TPB];     // token exists and is not text
-    if (threadIdx.x < ROPE_TPB) {
-        const int64_t row = row0 + threadIdx.x;
-        rotate[threadIdx.x] = row < rows && (row % n_tokens) >= r.n_prefix;
-    }
-    __syncthreads();
-
+    const int ntok = (int)(rows - row0 < ROPE_TPB ? rows - row0 : ROPE_TPB);   // >= 1
     const int dpr = head_dim / EPC;      // chunks per head row
     const int cpr = heads * dpr;         // chunks per token row
-    // walk (token, tensor, chunk) with the chunk index fastest
+    // the tensors present (the host passes at least one), q first
+    uint4* const ten0 = q != nullptr ? q : k;
+    uint4* const ten1 = q != nullptr ? k : nullptr;
+    const int nten = ten1 != nullptr ? 2 : 1;
+
     int c = threadIdx.x, which = 0, tk = 0;
-    while (c >= cpr) { c -= cpr; if (++which == 2) { which = 0; ++tk; } }
-    for (; tk < ROPE_TPB;) {
-        const int64_t row = row0 + tk;
-        uint4* base = which ? k : q;
-        if (base != nullptr && rotate[tk]) {
-            uint4* p = base + row * cpr + c;
-            uint4 v = *p;
-            const f32x2_t* t = cs + tk * half + (c % dpr) * (EPC / 2);
+    auto advance = [&]() {
+        c += 256;
+        while (c >= cpr) { c -= cpr; if (++which == nten) { which = 0; ++tk; } }
+    };
+    while (c >= cpr) { c -= cpr; if (++which == nten) { which = 0; ++tk; } }
+
+    uint4 v[ROPE_BATCH];
+    uint4* ptr[ROPE_BATCH];
+    int slot[ROPE_BATCH];                // tk * half + first pair of the chunk; -1: none
+    auto load_batch = [&]() {
+#pragma unroll
+        for (int u = 0; u < ROPE_BATCH; ++u) {
+            slot[u] = -1;
+            if (tk < ntok) {
+                ptr[u] = (which ? ten1 : ten0) + (row0 + tk) * cpr + c;
+                v[u] = *ptr[u];
+                slot[u] = tk * half + (c % dpr) * (EPC / 2);
+            }
+            advance();
+        }
+    };
+    auto rotate_store_batch = [&]() {
+#pragma unroll
+        for (int u = 0; u < ROPE_BATCH; ++u) {
+            if (slot[u] < 0 || !rotate[slot[u] / half]) continue;
+            const f32x2_t* t = cs + slot[u];
+            uint4 w4 = v[u];
             if constexpr (BF16) {
-                uint32_t w[4] = {v.x, v.y, v.z, v.w};
+                uint32_t w[4] = {w4.x, w4.y, w4.z, w4.w};
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
                     float a = bf16_lo(w[m]), b = bf16_hi(w[m]);
@@ -71,22 +89,38 @@ void rope3d_kernel(uint4* q, uint4* k, int64_t rows, int64_t n_tokens, int heads
                     rope_rotate(a, b, e.x, e.y);
                     w[m] = pack_bf16x2(a, b);
                 }
-                v = uint4{w[0], w[1], w[2], w[3]};
+                w4 = uint4{w[0], w[1], w[2], w[3]};
             } else {
-                float f[4] = {__uint_as_float(v.x), __uint_as_float(v.y),
-                              __uint_as_float(v.z), __uint_as_float(v.w)};
+                float f[4] = {__uint_as_float(w4.x), __uint_as_float(w4.y),
+                              __uint_as_float(w4.z), __uint_as_float(w4.w)};
 #pragma unroll
                 for (int m = 0; m < 2; ++m) {
                     const f32x2_t e = t[m];
                     rope_rotate(f[2 * m], f[2 * m + 1], e.x, e.y);
                 }
-                v = uint4{__float_as_uint(f[0]), __float_as_uint(f[1]),
-                          __float_as_uint(f[2]), __float_as_uint(f[3])};
+                w4 = uint4{__float_as_uint(f[0]), __float_as_uint(f[1]),
+                           __float_as_uint(f[2]), __float_as_uint(f[3])};
             }
-            *p = v;
+            *ptr[u] = w4;
         }
-        c += 256;
-        while (c >= cpr) { c -= cpr; if (++which == 2) { which = 0; ++tk; } }
+    };
+
+    load_batch();
+    for (int i = threadIdx.x; i < ROPE_TPB * half; i += 256) {
+        const int t = i / half, pair = i - t * half;
+        float cv = 1.f, sv = 0.f;
+        int tp, hp, wp;
+        if (t < ntok && rope_token_pos(r, (row0 + t) % n_tokens, &tp, &hp, &wp))
+            rope_cos_sin(r, rope_pair_pos(r, pair, tp, hp, wp), pair, &cv, &sv);
+        cs[i] = f32x2_t{cv, sv};
+    }
+    if (threadIdx.x < ROPE_TPB)
+        rotate[threadIdx.x] = (int)threadIdx.x < ntok && ((row0 + threadIdx.x) % n_tokens) >= r.n_prefix;
+    __syncthreads();
+    rotate_store_batch();
+    while (tk < ntok) {
+        load_batch();
+        rotate_store_batch();
     }
 }
 
