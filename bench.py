@@ -311,9 +311,10 @@ def main():
             what="torch.addcmul over the same x, shift, scale and y (3 reads + 1 write, bf16), "
                  "100 launches: plain elementwise streaming of AdaLN's bytes on this box")
     if rep_rope_stream is not None:
+        k_bytes = 2 * tk.numel() * tk.element_size()       # all of K, read and written
         kernels["rope_pattern_reference"] = dict(
             rep_rope_stream, hbm_frac=round(
-                rope_bytes / (rep_rope_stream["median_ms"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                k_bytes / (rep_rope_stream["median_ms"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
             what="torch.mul_(1) on K in place (1 read + 1 write, bf16), 100 launches: plain "
                  "elementwise streaming of RoPE's bytes on this box")
     kernels["rope_100"] = dict(rep_rope, hbm_frac=round(
