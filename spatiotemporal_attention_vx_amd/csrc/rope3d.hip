@@ -27,15 +27,17 @@ constexpr int ROPE_MAX_HALF = ROPE_MAX_PAIRS;
 
 // Adjacent pairs.  Every thread owns the (token, tensor, chunk) items
 // threadIdx.x + 256 j of its workgroup, chunk index fastest, and handles
-// them ROPE_BATCH at a time: all loads of a batch are issued before any
-// chunk is rotated and stored, so each thread keeps ROPE_BATCH 16-byte loads
-// in flight (a load issued after a store to another chunk could not be moved
-// above it).  The first batch is loaded before the angles are evaluated, so
-// the sin/cos work runs under those loads.  Text-prefix rows are read but
-// never written.
-constexpr int ROPE_BATCH = 8;
+// them BATCH at a time: all loads of a batch are issued before any chunk is
+// rotated and stored, so each thread keeps BATCH 16-byte loads in flight (a
+// load issued after a store to another chunk could not be moved above it).
+// The first batch is loaded before the angles are evaluated, so the sin/cos
+// work runs under those loads.  Text-prefix rows are read but never written.
+// BATCH is 8 when every thread has at least 8 chunks (wide token rows), else
+// 4: eight loads in flight need 87 VGPRs (5 waves per SIMD) against 56 (8
+// waves), and rows of a few heads gain more from occupancy than from depth.
+constexpr int ROPE_BATCH = 4;        // head-half kernel: loads in flight per thread
 
-template <bool BF16>
+template <bool BF16, int BATCH>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256)))
 void rope3d_kernel(uint4* q, uint4* k, int64_t rows, int64_t n_tokens, int heads,
                    int head_dim, RopeArgs r) {
@@ -59,24 +61,26 @@ void rope3d_kernel(uint4* q, uint4* k, int64_t rows, int64_t n_tokens, int heads
     };
     while (c >= cpr) { c -= cpr; if (++which == nten) { which = 0; ++tk; } }
 
-    uint4 v[ROPE_BATCH];
-    uint4* ptr[ROPE_BATCH];
-    int slot[ROPE_BATCH];                // tk * half + first pair of the chunk; -1: none
+    uint4 v[BATCH];
+    uint4* ptr[BATCH];
+    int slot[BATCH];                     // tk * half + first pair of the chunk; -1: none
     auto load_batch = [&]() {
 #pragma unroll
-        for (int u = 0; u < ROPE_BATCH; ++u) {
-            slot[u] = -1;
-            if (tk < ntok) {
-                ptr[u] = (which ? ten1 : ten0) + (row0 + tk) * cpr + c;
-                v[u] = *ptr[u];
-                slot[u] = tk * half + (c % dpr) * (EPC / 2);
-            }
+        for (int u = 0; u < BATCH; ++u) slot[u] = -1;
+        // stop at the workgroup's last item: with few heads a thread has only
+        // one or two, and walking past them would cost more than the loads
+#pragma unroll
+        for (int u = 0; u < BATCH; ++u) {
+            if (tk >= ntok) break;
+            ptr[u] = (which ? ten1 : ten0) + (row0 + tk) * cpr + c;
+            v[u] = *ptr[u];
+            slot[u] = tk * half + (c % dpr) * (EPC / 2);
             advance();
         }
     };
     auto rotate_store_batch = [&]() {
 #pragma unroll
-        for (int u = 0; u < ROPE_BATCH; ++u) {
+        for (int u = 0; u < BATCH; ++u) {
             if (slot[u] < 0 || !rotate[slot[u] / half]) continue;
             const f32x2_t* t = cs + slot[u];
             uint4 w4 = v[u];
@@ -238,55 +242,83 @@ void rope3d_split_kernel(uint4* q, uint4* k, int64_t rows, int64_t n_tokens, int
 // Halves of the head (pairing 1) when head_dim / 2 is a whole number of
 // 16-byte chunks: element m of chunk c (c < half the row's chunks) pairs with
 // element m of chunk c + dpr / 2, so a thread loads both chunks and rotates
-// in registers, with the angle of pair c * EPC + m.
+// in registers, with the angle of pair c * EPC + m.  As in the adjacent
+// kernel, a thread handles its chunk pairs ROPE_BATCH / 2 at a time with all
+// loads of a batch issued first, the first batch before the angles.
 template <bool BF16>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256)))
 void rope3d_halves_kernel(uint4* q, uint4* k, int64_t rows, int64_t n_tokens, int heads,
                           int head_dim, RopeArgs r) {
     constexpr int EPC = BF16 ? 8 : 4;
+    constexpr int U = ROPE_BATCH / 2;    // chunk pairs per batch: ROPE_BATCH loads in flight
     __shared__ f32x2_t cs[ROPE_TPB * ROPE_MAX_HALF];
     __shared__ int rotate[ROPE_TPB];
     const int half = head_dim >> 1;
     const int64_t row0 = (int64_t)blockIdx.x * ROPE_TPB;
-    for (int i = threadIdx.x; i < ROPE_TPB * half; i += 256) {
-        const int tk = i / half, pair = i - tk * half;
-        const int64_t row = row0 + tk;
-        float c = 1.f, s = 0.f;
-        int tp, hp, wp;
-        if (row < rows && rope_token_pos(r, row % n_tokens, &tp, &hp, &wp))
-            rope_cos_sin(r, rope_pair_pos(r, pair, tp, hp, wp), pair, &c, &s);
-        cs[i] = f32x2_t{c, s};
-    }
-    if (threadIdx.x < ROPE_TPB) {
-        const int64_t row = row0 + threadIdx.x;
-        rotate[threadIdx.x] = row < rows && (row % n_tokens) >= r.n_prefix;
-    }
-    __syncthreads();
-
+    const int ntok = (int)(rows - row0 < ROPE_TPB ? rows - row0 : ROPE_TPB);   // >= 1
     const int dpr = head_dim / EPC, hc = dpr / 2;   // chunks per head row, and per half
-    const int per_token = heads * hc;                // chunk pairs per token row
-    // walk (token, tensor, head, chunk pair) with the chunk pair fastest
-    for (int u = threadIdx.x; u < ROPE_TPB * 2 * per_token; u += 256) {
-        const int tw = u / per_token, rem = u - tw * per_token;
-        const int which = tw & 1, tk = tw >> 1;
-        const int h = rem / hc, c = rem - h * hc;
-        uint4* base = which ? k : q;
-        if (base == nullptr || !rotate[tk]) continue;
-        uint4* p0 = base + ((row0 + tk) * heads + h) * dpr + c;
-        uint4* p1 = p0 + hc;
-        const uint4 v0 = *p0, v1 = *p1;
-        float f0[EPC], f1[EPC];
-        unpack_chunk<BF16>(u32x4_t{v0.x, v0.y, v0.z, v0.w}, f0);
-        unpack_chunk<BF16>(u32x4_t{v1.x, v1.y, v1.z, v1.w}, f1);
-        const f32x2_t* t = cs + tk * half + c * EPC;
+    const int per_token = heads * hc;                // chunk pairs per token row and tensor
+    uint4* const ten0 = q != nullptr ? q : k;
+    uint4* const ten1 = q != nullptr ? k : nullptr;
+    const int nten = ten1 != nullptr ? 2 : 1;
+    const int items = ntok * nten * per_token;
+    // items (token, tensor, head, chunk pair) with the chunk pair fastest;
+    // this thread's are threadIdx.x + 256 j, handled U at a time, loads first
+    int u = threadIdx.x;
+    uint4 v0[U], v1[U];
+    uint4* ptr[U];
+    int slot[U];                          // tk * half + first pair of the chunk; -1: none
+    auto load_batch = [&]() {
 #pragma unroll
-        for (int m = 0; m < EPC; ++m) {
-            const f32x2_t e = t[m];
-            rope_rotate(f0[m], f1[m], e.x, e.y);
+        for (int j = 0; j < U; ++j) {
+            slot[j] = -1;
+            if (u < items) {
+                const int tw = u / per_token, rem = u - tw * per_token;
+                const int tk = tw / nten, which = tw - tk * nten;
+                const int h = rem / hc, c = rem - h * hc;
+                ptr[j] = (which ? ten1 : ten0) + ((row0 + tk) * heads + h) * dpr + c;
+                v0[j] = ptr[j][0];
+                v1[j] = ptr[j][hc];
+                slot[j] = tk * half + c * EPC;
+            }
+            u += 256;
         }
-        const u32x4_t w0 = pack_chunk<BF16>(f0), w1 = pack_chunk<BF16>(f1);
-        *p0 = uint4{w0[0], w0[1], w0[2], w0[3]};
-        *p1 = uint4{w1[0], w1[1], w1[2], w1[3]};
+    };
+    auto rotate_store_batch = [&]() {
+#pragma unroll
+        for (int j = 0; j < U; ++j) {
+            if (slot[j] < 0 || !rotate[slot[j] / half]) continue;
+            float f0[EPC], f1[EPC];
+            unpack_chunk<BF16>(u32x4_t{v0[j].x, v0[j].y, v0[j].z, v0[j].w}, f0);
+            unpack_chunk<BF16>(u32x4_t{v1[j].x, v1[j].y, v1[j].z, v1[j].w}, f1);
+            const f32x2_t* t = cs + slot[j];
+#pragma unroll
+            for (int m = 0; m < EPC; ++m) {
+                const f32x2_t e = t[m];
+                rope_rotate(f0[m], f1[m], e.x, e.y);
+            }
+            const u32x4_t w0 = pack_chunk<BF16>(f0), w1 = pack_chunk<BF16>(f1);
+            ptr[j][0] = uint4{w0[0], w0[1], w0[2], w0[3]};
+            ptr[j][hc] = uint4{w1[0], w1[1], w1[2], w1[3]};
+        }
+    };
+
+    load_batch();
+    for (int i = threadIdx.x; i < ROPE_TPB * half; i += 256) {
+        const int t = i / half, pair = i - t * half;
+        float cv = 1.f, sv = 0.f;
+        int tp, hp, wp;
+        if (t < ntok && rope_token_pos(r, (row0 + t) % n_tokens, &tp, &hp, &wp))
+            rope_cos_sin(r, rope_pair_pos(r, pair, tp, hp, wp), pair, &cv, &sv);
+        cs[i] = f32x2_t{cv, sv};
+    }
+    if (threadIdx.x < ROPE_TPB)
+        rotate[threadIdx.x] = (int)threadIdx.x < ntok && ((row0 + threadIdx.x) % n_tokens) >= r.n_prefix;
+    __syncthreads();
+    rotate_store_batch();
+    while (u < items) {
+        load_batch();
+        rotate_store_batch();
     }
 }
 
@@ -313,12 +345,22 @@ hipError_t launch_rope3d(void* q, void* k, int64_t batch, int64_t n_tokens, int6
                                (uint4*)q, (uint4*)k, rows, n_tokens, (int)heads, (int)head_dim, r);
         return hipGetLastError();
     }
-    if (bf16)
-        hipLaunchKernelGGL(rope3d_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, st,
-                           (uint4*)q, (uint4*)k, rows, n_tokens, (int)heads, (int)head_dim, r);
+    // chunks per thread in a full workgroup: ROPE_TPB tokens x tensors x chunks per row
+    const int64_t per_thread = ROPE_TPB * ((q != nullptr) + (k != nullptr)) * heads *
+                               (head_dim / epc) / 256;
+    const dim3 grid((unsigned)blocks), block(256);
+    if (bf16 && per_thread >= 8)
+        hipLaunchKernelGGL((rope3d_kernel<true, 8>), grid, block, 0, st, (uint4*)q, (uint4*)k,
+                           rows, n_tokens, (int)heads, (int)head_dim, r);
+    else if (bf16)
+        hipLaunchKernelGGL((rope3d_kernel<true, 4>), grid, block, 0, st, (uint4*)q, (uint4*)k,
+                           rows, n_tokens, (int)heads, (int)head_dim, r);
+    else if (per_thread >= 8)
+        hipLaunchKernelGGL((rope3d_kernel<false, 8>), grid, block, 0, st, (uint4*)q, (uint4*)k,
+                           rows, n_tokens, (int)heads, (int)head_dim, r);
     else
-        hipLaunchKernelGGL(rope3d_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, st,
-                           (uint4*)q, (uint4*)k, rows, n_tokens, (int)heads, (int)head_dim, r);
+        hipLaunchKernelGGL((rope3d_kernel<false, 4>), grid, block, 0, st, (uint4*)q, (uint4*)k,
+                           rows, n_tokens, (int)heads, (int)head_dim, r);
     return hipGetLastError();
 }
 

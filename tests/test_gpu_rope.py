@@ -45,6 +45,10 @@ def test_workload(gpu_lib, name):
     ("bf16", (2, 2, 2), 1, 2, 8, 1, (2, 2, 4)),
     ("bf16", (2, 4, 3), 0, 1, 256, 3, (64, 96, 96)),
     ("bf16", (5, 2, 3), 3, 2, 96, 1, (0, 48, 48)),
+    # wide token rows (8 or more chunks per thread of a 4-token workgroup): the
+    # eight-deep load batches, with a ragged last workgroup, a prefix, batch 2
+    ("bf16", (3, 5, 7), 2, 40, 128, 2, (44, 42, 42)),
+    ("f32", (2, 3, 5), 3, 32, 128, 1, (44, 42, 42)),
 ])
 def test_ragged(gpu_lib, dtype, grid, prefix, heads, d, batch, split):
     import torch
