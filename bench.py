@@ -249,7 +249,7 @@ def main():
                   (lambda: binding.adaln_modulate_ex(tx, tsh, tsc, ty, wl.eps, stream=stream)))
     rep_adaln = reps(adaln_call)
     rep_rope = reps(lambda: binding.rope3d_apply(None if fused else tq, tk, desc, stream=stream))
-    # Reference for AdaLN's access pattern on this machine: torch's own elementwise
+    # Reference for AdaLN's access pattern on this GPU: torch's own elementwise
     # kernel streaming the same four tensors (three read, one written), timed
     # the same way.  Not part of the step.
     rep_stream = (reps(lambda: torch.addcmul(tsh, tx, tsc, out=ty))
@@ -259,7 +259,7 @@ def main():
     rep_rope_stream = reps(lambda: tk.mul_(1)) if fused else None
 
     # The bf16 MFMA rate this chip sustains on the same kind of data: a pure
-    # v_mfma loop timed on this machine right after the step (its clock is set by
+    # v_mfma loop timed on this GPU right after the step (its clock is set by
     # the power limit, which depends on the operand data).
     # It is a reference beside the metric, so a failure here is reported in the
     # line instead of ending the run.
@@ -309,14 +309,14 @@ def main():
             rep_stream, hbm_frac=round(
                 adaln_bytes / (rep_stream["median_ms"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
             what="torch.addcmul over the same x, shift, scale and y (3 reads + 1 write, bf16), "
-                 "100 launches: plain elementwise streaming of AdaLN's bytes on this box")
+                 "100 launches: plain elementwise streaming of AdaLN's bytes on this GPU")
     if rep_rope_stream is not None:
         k_bytes = 2 * tk.numel() * tk.element_size()       # all of K, read and written
         kernels["rope_pattern_reference"] = dict(
             rep_rope_stream, hbm_frac=round(
                 k_bytes / (rep_rope_stream["median_ms"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
             what="torch.mul_(1) on K in place (1 read + 1 write, bf16), 100 launches: plain "
-                 "elementwise streaming of RoPE's bytes on this box")
+                 "elementwise streaming of RoPE's bytes on this GPU")
     kernels["rope_100"] = dict(rep_rope, hbm_frac=round(
         rope_bytes / (rep_rope["median_ms"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4))
     if split:
@@ -370,7 +370,7 @@ def main():
                 "attn_frac_of_ceiling": round(attn_tflops / ceiling["tflops"], 4),
                 "what": ("pure v_mfma_f32_32x32x16_bf16 loop on "
                          + ("all-zero" if args.inputs == "zeros" else "N(0,1) bf16")
-                         + f" operands, {ceiling['launch']}, same box, same run: the rate the "
+                         + f" operands, {ceiling['launch']}, same GPU, same run: the rate the "
                            "chip's power limit allows on this data"),
             } if "tflops" in ceiling else None),
             **({"measured_ceiling_error": ceiling["error"]} if "error" in ceiling else {}),
