@@ -46,7 +46,7 @@ typedef enum {
     VX_OK = 0,
     VX_ERR_NULL = 1,        /* a required pointer is NULL                     */
     VX_ERR_INVALID = 2,     /* sizes or parameters inconsistent or out of range */
-    VX_ERR_UNSUPPORTED = 3, /* valid, but not a shape/dtype this build serves  */
+    VX_ERR_UNSUPPORTED = 3, /* valid, but not a shape/dtype this library serves */
     VX_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned                */
     VX_ERR_HIP = 5          /* the HIP runtime reported an error at launch     */
 } vx_status;
