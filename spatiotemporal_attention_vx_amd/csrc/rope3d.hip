@@ -25,6 +25,31 @@ namespace vx {
 constexpr int ROPE_TPB = 4;          // tokens per workgroup
 constexpr int ROPE_MAX_HALF = ROPE_MAX_PAIRS;
 
+// Q and K rows are read once and written once.  When the rotated tensors
+// are much larger than the 256 MiB memory-side cache (NT), non-temporal
+// accesses keep them from displacing what is cached and from leaving dirty
+// lines behind: the large workload's K (774 MB) then rotates at 76% of HBM
+// in the hot path instead of 74%, and 72% instead of 66% back to back.
+// Smaller tensors gain from staying partly cached between launches (K of
+// 277-528 MB: 77-82% in the hot path with plain accesses, 75-78% with
+// non-temporal ones), so the host picks NT by size.
+constexpr int64_t ROPE_NT_BYTES = int64_t(640) << 20;   // 2.5 x the memory-side cache
+
+template <bool NT>
+__device__ __forceinline__ uint4 stream_load(const uint4* p) {
+    if constexpr (NT) {
+        const u32x4_t v = __builtin_nontemporal_load((const u32x4_t*)p);
+        return uint4{v[0], v[1], v[2], v[3]};
+    } else {
+        return *p;
+    }
+}
+template <bool NT>
+__device__ __forceinline__ void stream_store(uint4* p, const uint4& v) {
+    if constexpr (NT) __builtin_nontemporal_store(u32x4_t{v.x, v.y, v.z, v.w}, (u32x4_t*)p);
+    else *p = v;
+}
+
 // Adjacent pairs.  Every thread owns the (token, tensor, chunk) items
 // threadIdx.x + 256 j of its workgroup, chunk index fastest, and handles
 // them BATCH at a time: all loads of a batch are issued before any chunk is
@@ -37,7 +62,7 @@ constexpr int ROPE_MAX_HALF = ROPE_MAX_PAIRS;
 // waves), and rows of a few heads gain more from occupancy than from depth.
 constexpr int ROPE_BATCH = 4;        // head-half kernel: loads in flight per thread
 
-template <bool BF16, int BATCH>
+template <bool BF16, int BATCH, bool NT>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256)))
 void rope3d_kernel(uint4* q, uint4* k, int64_t rows, int64_t n_tokens, int heads,
                    int head_dim, RopeArgs r) {
@@ -73,7 +98,7 @@ void rope3d_kernel(uint4* q, uint4* k, int64_t rows, int64_t n_tokens, int heads
         for (int u = 0; u < BATCH; ++u) {
             if (tk >= ntok) break;
             ptr[u] = (which ? ten1 : ten0) + (row0 + tk) * cpr + c;
-            v[u] = *ptr[u];
+            v[u] = stream_load<NT>(ptr[u]);
             slot[u] = tk * half + (c % dpr) * (EPC / 2);
             advance();
         }
@@ -105,7 +130,7 @@ void rope3d_kernel(uint4* q, uint4* k, int64_t rows, int64_t n_tokens, int heads
                 w4 = uint4{__float_as_uint(f[0]), __float_as_uint(f[1]),
                            __float_as_uint(f[2]), __float_as_uint(f[3])};
             }
-            *ptr[u] = w4;
+            stream_store<NT>(ptr[u], w4);
         }
     };
 
@@ -154,7 +179,7 @@ __device__ __forceinline__ void wave_sync_lds() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-template <bool BF16>
+template <bool BF16, bool NT>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256)))
 void rope3d_split_kernel(uint4* q, uint4* k, int64_t rows, int64_t n_tokens, int heads,
                          int head_dim, RopeArgs r) {
@@ -208,7 +233,7 @@ void rope3d_split_kernel(uint4* q, uint4* k, int64_t rows, int64_t n_tokens, int
             uint4* base = u < heads ? q : k;
             const int h = u < heads ? u : u - heads;
             ptr[i] = live ? base + row * dpt + (int64_t)h * dpr + c : nullptr;
-            if (live) raw[i] = *ptr[i];
+            if (live) raw[i] = stream_load<NT>(ptr[i]);
         }
 #pragma unroll
         for (int i = 0; i < U; ++i)
@@ -233,7 +258,7 @@ void rope3d_split_kernel(uint4* q, uint4* k, int64_t rows, int64_t n_tokens, int
                 out[m] = rope_rotate_elem(f[m], xp, (second >> m) & 1, cr[m], sr[m]);
             }
             const u32x4_t w = pack_chunk<BF16>(out);
-            *ptr[i] = uint4{w[0], w[1], w[2], w[3]};
+            stream_store<NT>(ptr[i], uint4{w[0], w[1], w[2], w[3]});
         }
         wave_sync_lds();   // this pass's reads are done before the next pass writes
     }
@@ -245,7 +270,7 @@ void rope3d_split_kernel(uint4* q, uint4* k, int64_t rows, int64_t n_tokens, int
 // in registers, with the angle of pair c * EPC + m.  As in the adjacent
 // kernel, a thread handles its chunk pairs ROPE_BATCH / 2 at a time with all
 // loads of a batch issued first, the first batch before the angles.
-template <bool BF16>
+template <bool BF16, bool NT>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256)))
 void rope3d_halves_kernel(uint4* q, uint4* k, int64_t rows, int64_t n_tokens, int heads,
                           int head_dim, RopeArgs r) {
@@ -277,8 +302,8 @@ void rope3d_halves_kernel(uint4* q, uint4* k, int64_t rows, int64_t n_tokens, in
                 const int tk = tw / nten, which = tw - tk * nten;
                 const int h = rem / hc, c = rem - h * hc;
                 ptr[j] = (which ? ten1 : ten0) + ((row0 + tk) * heads + h) * dpr + c;
-                v0[j] = ptr[j][0];
-                v1[j] = ptr[j][hc];
+                v0[j] = stream_load<NT>(ptr[j]);
+                v1[j] = stream_load<NT>(ptr[j] + hc);
                 slot[j] = tk * half + c * EPC;
             }
             u += 256;
@@ -298,8 +323,8 @@ void rope3d_halves_kernel(uint4* q, uint4* k, int64_t rows, int64_t n_tokens, in
                 rope_rotate(f0[m], f1[m], e.x, e.y);
             }
             const u32x4_t w0 = pack_chunk<BF16>(f0), w1 = pack_chunk<BF16>(f1);
-            ptr[j][0] = uint4{w0[0], w0[1], w0[2], w0[3]};
-            ptr[j][hc] = uint4{w1[0], w1[1], w1[2], w1[3]};
+            stream_store<NT>(ptr[j], uint4{w0[0], w0[1], w0[2], w0[3]});
+            stream_store<NT>(ptr[j] + hc, uint4{w1[0], w1[1], w1[2], w1[3]});
         }
     };
 
@@ -322,46 +347,51 @@ void rope3d_halves_kernel(uint4* q, uint4* k, int64_t rows, int64_t n_tokens, in
     }
 }
 
+// One launch of the kernel `kind` selects: 1 head halves, 2 band halves,
+// 8 or 4 adjacent pairs with that many loads in flight per thread.
+template <bool BF16, bool NT>
+hipError_t launch_rope_kind(int kind, dim3 grid, hipStream_t st, uint4* q, uint4* k, int64_t rows,
+                            int64_t n_tokens, int heads, int head_dim, const RopeArgs& r) {
+    const dim3 block(256);
+    if (kind == 1)
+        hipLaunchKernelGGL((rope3d_halves_kernel<BF16, NT>), grid, block, 0, st, q, k, rows,
+                           n_tokens, heads, head_dim, r);
+    else if (kind == 2)
+        hipLaunchKernelGGL((rope3d_split_kernel<BF16, NT>), grid, block, 0, st, q, k, rows,
+                           n_tokens, heads, head_dim, r);
+    else if (kind == 8)
+        hipLaunchKernelGGL((rope3d_kernel<BF16, 8, NT>), grid, block, 0, st, q, k, rows, n_tokens,
+                           heads, head_dim, r);
+    else
+        hipLaunchKernelGGL((rope3d_kernel<BF16, 4, NT>), grid, block, 0, st, q, k, rows, n_tokens,
+                           heads, head_dim, r);
+    return hipGetLastError();
+}
+
 hipError_t launch_rope3d(void* q, void* k, int64_t batch, int64_t n_tokens, int64_t heads,
                          int64_t head_dim, const RopeArgs& r, bool bf16, hipStream_t st) {
     const int64_t rows = batch * n_tokens;
-    const int64_t blocks = (rows + ROPE_TPB - 1) / ROPE_TPB;
+    const dim3 grid((unsigned)((rows + ROPE_TPB - 1) / ROPE_TPB));
     const int epc = bf16 ? 8 : 4;
+    const int ntens = (q != nullptr) + (k != nullptr);
+    int kind;
     if (r.pairing == 1 && (head_dim / 2) % epc == 0) {
-        if (bf16)
-            hipLaunchKernelGGL(rope3d_halves_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, st,
-                               (uint4*)q, (uint4*)k, rows, n_tokens, (int)heads, (int)head_dim, r);
-        else
-            hipLaunchKernelGGL(rope3d_halves_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, st,
-                               (uint4*)q, (uint4*)k, rows, n_tokens, (int)heads, (int)head_dim, r);
-        return hipGetLastError();
+        kind = 1;
+    } else if (r.pairing != 0) {
+        kind = 2;
+    } else {
+        // chunks per thread in a full workgroup: ROPE_TPB tokens x tensors x chunks per row
+        kind = ROPE_TPB * ntens * heads * (head_dim / epc) / 256 >= 8 ? 8 : 4;
     }
-    if (r.pairing != 0) {
-        if (bf16)
-            hipLaunchKernelGGL(rope3d_split_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, st,
-                               (uint4*)q, (uint4*)k, rows, n_tokens, (int)heads, (int)head_dim, r);
-        else
-            hipLaunchKernelGGL(rope3d_split_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, st,
-                               (uint4*)q, (uint4*)k, rows, n_tokens, (int)heads, (int)head_dim, r);
-        return hipGetLastError();
-    }
-    // chunks per thread in a full workgroup: ROPE_TPB tokens x tensors x chunks per row
-    const int64_t per_thread = ROPE_TPB * ((q != nullptr) + (k != nullptr)) * heads *
-                               (head_dim / epc) / 256;
-    const dim3 grid((unsigned)blocks), block(256);
-    if (bf16 && per_thread >= 8)
-        hipLaunchKernelGGL((rope3d_kernel<true, 8>), grid, block, 0, st, (uint4*)q, (uint4*)k,
-                           rows, n_tokens, (int)heads, (int)head_dim, r);
-    else if (bf16)
-        hipLaunchKernelGGL((rope3d_kernel<true, 4>), grid, block, 0, st, (uint4*)q, (uint4*)k,
-                           rows, n_tokens, (int)heads, (int)head_dim, r);
-    else if (per_thread >= 8)
-        hipLaunchKernelGGL((rope3d_kernel<false, 8>), grid, block, 0, st, (uint4*)q, (uint4*)k,
-                           rows, n_tokens, (int)heads, (int)head_dim, r);
-    else
-        hipLaunchKernelGGL((rope3d_kernel<false, 4>), grid, block, 0, st, (uint4*)q, (uint4*)k,
-                           rows, n_tokens, (int)heads, (int)head_dim, r);
-    return hipGetLastError();
+    // bytes of the rotated tensors (the host has checked that they fit int64)
+    const bool nt = ntens * rows * heads * head_dim * (bf16 ? 2 : 4) > ROPE_NT_BYTES;
+    uint4 *qq = (uint4*)q, *kk = (uint4*)k;
+    const int h = (int)heads, d = (int)head_dim;
+    if (bf16)
+        return nt ? launch_rope_kind<true, true>(kind, grid, st, qq, kk, rows, n_tokens, h, d, r)
+                  : launch_rope_kind<true, false>(kind, grid, st, qq, kk, rows, n_tokens, h, d, r);
+    return nt ? launch_rope_kind<false, true>(kind, grid, st, qq, kk, rows, n_tokens, h, d, r)
+              : launch_rope_kind<false, false>(kind, grid, st, qq, kk, rows, n_tokens, h, d, r);
 }
 
 }  // namespace vx

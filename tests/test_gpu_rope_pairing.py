@@ -138,3 +138,33 @@ def test_large_grid_half_split(gpu_lib, pairing):
     wl = configs.SP_WORKLOADS["large_sp8"]
     say(f"attn workload {wl.name} pairing={pairing}")
     _workload_attention(wl, pairing)
+
+
+@pytest.mark.parametrize("pairing", [0, 1, 2])
+def test_streaming_size_every_pairing(gpu_lib, pairing):
+    """K of the 75,600-token workload alone (774 MB) is above the size from
+    which the kernels stream with non-temporal accesses, and Q and K of the
+    mid workload together (671 MB) just below it: each pairing's kernel is
+    checked on both sides, on 4096 seeded rows plus the first and last."""
+    import torch
+    for name, both in (("large", False), ("mid", True)):
+        wl = configs.WORKLOADS[name]
+        say(f"rope streaming size {name} pairing={pairing} q_and_k={both}")
+        q, k, _ = inputs.attention_inputs(wl)
+        desc = binding.RopeDesc.of(wl.grid, wl.split, wl.theta, wl.n_prefix, pairing)
+        tq, tk = dev(q), dev(k)
+        binding.rope3d_apply(tq if both else None, tk, desc)
+        torch.cuda.synchronize()
+        g = np.random.default_rng(1000 + pairing)
+        rows = np.unique(np.concatenate([[0, wl.n_tokens - 1],
+                                         g.choice(wl.n_tokens, 4096, replace=False)]))
+        for src, t, nm in (((q, tq, "q"),) if both else ()) + ((k, tk, "k"),):
+            got = host(t)[0, rows]
+            ref = oracle.rope3d_apply(inputs.values(src[0, rows]).astype(np.float64), wl.grid,
+                                      wl.split, wl.theta, wl.n_prefix, tokens=rows,
+                                      pairing=pairing)
+            check(got, ref, wl.dtype, f"rope {name} pairing {pairing} {nm}")
+        if not both:
+            np.testing.assert_array_equal(bits(tq), q.view(np.int16))   # Q untouched
+        del tq, tk
+        torch.cuda.empty_cache()
