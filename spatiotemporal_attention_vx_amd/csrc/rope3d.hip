@@ -7,11 +7,13 @@
 // one documented on vx_rope3d_desc.
 //
 // HBM-bound: each rotated row of Q and K is read and written once.  A
-// workgroup owns TPB consecutive tokens.  It first evaluates cos/sin of the
+// workgroup owns TPB consecutive tokens.  It evaluates cos/sin of the
 // head_dim/2 angles of each token into LDS (angles are shared by every head
-// and by Q and K, so they cost one evaluation per token and pair), then
-// streams the 16-byte chunks of the tokens' Q and K rows, consecutive lanes
-// on consecutive chunks.  With adjacent pairs (pairing 0) both elements of
+// and by Q and K, so they cost one evaluation per token and pair) while the
+// first loads of the tokens' rows are in flight, then streams the 16-byte
+// chunks of the Q and K rows, consecutive lanes on consecutive chunks, each
+// thread with several loads in flight; rows far larger than the memory-side
+// cache are read and written with non-temporal accesses.  With adjacent pairs (pairing 0) both elements of
 // a pair sit in one chunk.  With halves of the head (pairing 1) the two
 // elements sit in chunks c and c + (chunks per row) / 2 whenever head_dim / 2
 // is a whole number of chunks, and one thread rotates that chunk pair.
