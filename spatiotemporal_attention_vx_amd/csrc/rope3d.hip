@@ -385,8 +385,9 @@ hipError_t launch_rope3d(void* q, void* k, int64_t batch, int64_t n_tokens, int6
         // chunks per thread in a full workgroup: ROPE_TPB tokens x tensors x chunks per row
         kind = ROPE_TPB * ntens * heads * (head_dim / epc) / 256 >= 8 ? 8 : 4;
     }
-    // bytes of the rotated tensors (the host has checked that they fit int64)
-    const bool nt = ntens * rows * heads * head_dim * (bf16 ? 2 : 4) > ROPE_NT_BYTES;
+    // bytes of the rotated tensors; one tensor's count fits int64 (checked by
+    // the host), so compare per tensor rather than multiply by ntens
+    const bool nt = rows * heads * head_dim * (bf16 ? 2 : 4) > ROPE_NT_BYTES / ntens;
     uint4 *qq = (uint4*)q, *kk = (uint4*)k;
     const int h = (int)heads, d = (int)head_dim;
     if (bf16)
