@@ -17,7 +17,7 @@
 // belongs to lane g % 64, so every load instruction of a wave covers a
 // contiguous span.  Each lane issues all its loads up front (the row stays
 // in registers; when x and both tables together would take more than ~200
-// registers per lane, e.g. f32 tables at width 5120, only x is held and the
+// registers per lane, e.g. f32 tables at width 8192, only x is held and the
 // table loads wait for the output pass), then forms exact (count, mean, M2) statistics for each of
 // its groups and merges them with Chan's pairwise update (the parallel
 // form of Welford's algorithm): first across its groups, then across the
