@@ -32,10 +32,9 @@ convention is parity unpinned; the invariants pin everything else.
 """
 from .adaln import adaln_modulate, adaln_modulate_per_sample, layer_norm
 from .rope3d import token_positions, rope_angles, rope3d_apply
-from .attention import attention, attention_masked, attention_rope, merge_lse, softmax_rows
+from .attention import attention, attention_masked, attention_rope, merge_lse
 
 __all__ = [
     "adaln_modulate", "adaln_modulate_per_sample", "layer_norm", "token_positions", "rope_angles",
     "rope3d_apply", "attention", "attention_masked", "attention_rope", "merge_lse",
-    "softmax_rows",
 ]

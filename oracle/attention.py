@@ -35,13 +35,6 @@ import numpy as np
 from .rope3d import rope3d_apply
 
 
-def softmax_rows(s) -> np.ndarray:
-    """Row-wise softmax of a float64 score matrix (max subtracted first)."""
-    s = np.asarray(s, dtype=np.float64)
-    e = np.exp(s - s.max(axis=-1, keepdims=True))
-    return e / e.sum(axis=-1, keepdims=True)
-
-
 def attention(q, k, v, scale: float = 0.0, rows=None, row_block: int = 512):
     """Attention outputs for the query rows ``rows`` (default: all).
 

@@ -46,10 +46,27 @@ def test_lse_is_library_logsumexp():
 
 
 def test_softmax_rows_sum_to_one():
+    """The weights attention() applies sum to 1 in every row: with every value
+    equal to 1 each output element is that row's sum of weights.  Scores up to
+    about +-40 (q scaled by 10), so the max subtraction matters."""
     g = np.random.default_rng(3)
-    p = oracle.softmax_rows(g.standard_normal((20, 300)) * 10)
-    np.testing.assert_allclose(p.sum(axis=1), 1.0, atol=1e-12)
+    q, k = g.standard_normal((20, 2, 64)) * 10, g.standard_normal((300, 2, 64))
+    o, _ = oracle.attention(q, k, np.ones((300, 2, 64)))
+    np.testing.assert_allclose(o, 1.0, rtol=0, atol=1e-12)
+
+
+def test_weights_are_the_library_softmax():
+    """With V the identity (d = N, value j = unit vector e_j) attention()
+    returns its weight matrix itself: each row must equal scipy's softmax of
+    the scaled scores, be non-negative, and sum to 1."""
+    g = np.random.default_rng(13)
+    n = 48
+    q, k = g.standard_normal((n, 1, n)) * 3, g.standard_normal((n, 1, n))
+    p, _ = oracle.attention(q, k, np.eye(n)[:, None, :], scale=0.4)
+    ref = scipy.special.softmax(0.4 * (q[:, 0] @ k[:, 0].T), axis=1)
+    np.testing.assert_allclose(p[:, 0], ref, rtol=0, atol=1e-14)
     assert (p >= 0).all()
+    np.testing.assert_allclose(p.sum(axis=2), 1.0, rtol=0, atol=1e-12)
 
 
 def test_equal_keys_give_mean_of_values():
