@@ -60,12 +60,8 @@ def parse():
     p.add_argument("--kv-split", type=int, default=0,
                    help="run attention as two key parts [0, S) and [S, N) merged through their "
                         "LSEs (vx_flash_attn_fwd_kv twice + vx_attn_merge2); 0 = one call")
-    p.add_argument("--cpu-rows", type=int, default=512,
+    p.add_argument("--cpu-rows", type=int, default=1024,
                    help="query rows of the oracle CPU baseline (0 = skip it)")
-    p.add_argument("--inputs", choices=["normal", "zeros"], default="normal",
-                   help="normal: the workload's seeded N(0,1) tensors (the metric); zeros: "
-                        "every input set to zero on the GPU, a power diagnosis only (the "
-                        "kernels run the same instructions; the line is marked diagnostic)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run a plain 1 GiB elementwise copy (HBM counter calibration)")
     return p.parse_args()
@@ -85,7 +81,7 @@ def measured_traffic(wl, args, pairing):
     import hashlib
     path = os.path.join(ROOT, "profiles", "attention_large_traffic.json")
     if (wl.name != "large" or args.kv_split or args.rope != "fused" or pairing != 0
-            or getattr(args, "inputs", "normal") != "normal" or not os.path.exists(path)):
+            or not os.path.exists(path)):
         return None
     with open(path) as f:
         rec = json.load(f)
@@ -95,27 +91,71 @@ def measured_traffic(wl, args, pairing):
     return rec["bytes_per_launch"]
 
 
-def cpu_baseline(wl, q, k, v, rows_count, pairing=0):
-    """The oracle, as it stands, on `rows_count` query rows x all heads x all keys."""
-    import numpy as np
+# Inputs of the CPU baseline, set before its worker processes are forked so
+# that they inherit them (copy on write) instead of receiving copies.
+_CPU_JOB = {}
+
+
+def _oracle_head(h):
+    """Worker: the oracle on head h, every sampled query row."""
+    import threadpoolctl
     import oracle
+    j = _CPU_JOB
+    wl = j["wl"]
+    with threadpoolctl.threadpool_limits(1):
+        oracle.attention_rope(j["q"][:, h:h + 1], j["k"][:, h:h + 1], j["v"][:, h:h + 1], wl.grid,
+                              wl.split, wl.theta, wl.n_prefix, rows=j["rows"],
+                              pairing=j["pairing"])
+    return j["rows"].size
+
+
+def _warm_worker(_):
+    """Untimed: one head's work in a fresh worker (its first call pays the page
+    faults of every buffer size the oracle allocates), then wait until every
+    worker holds one of these tasks, so that each worker takes exactly one."""
+    _oracle_head(0)
+    _CPU_JOB["barrier"].wait(timeout=600)
+    return 0
+
+
+def cpu_workers():
+    """Host processes the CPU baseline uses: the thread budget the host sets for
+    this job (OMP_NUM_THREADS) if any, else every core the OS reports."""
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    n = int(env) if env.isdigit() and int(env) > 0 else (os.cpu_count() or 1)
+    return max(1, min(n, os.cpu_count() or 1))
+
+
+def cpu_baseline(wl, q, k, v, rows_count, pairing=0):
+    """The oracle, as it stands, on `rows_count` query rows x all heads x all keys.
+
+    Heads are spread over a pool of forked worker processes, one per core of
+    the host's budget, each with one BLAS thread; the oracle itself is
+    unchanged.  Each worker first runs one head untimed (process start-up and
+    first-touch page faults are not the oracle's rate).  Call it before this
+    process initialises the GPU: the workers are forked from it."""
+    import concurrent.futures as cf
+    import multiprocessing as mp
     from spatiotemporal_attention_vx_amd import inputs
-    try:
-        import threadpoolctl
-        threads = max(i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()) or 1
-    except Exception:  # pragma: no cover
-        threads = os.cpu_count() or 1
     rows = inputs.sample_rows(wl, count=rows_count)
-    qv, kv, vv = inputs.values(q[0]), inputs.values(k[0]), inputs.values(v[0])
-    t0 = time.perf_counter()
-    oracle.attention_rope(qv, kv, vv, wl.grid, wl.split, wl.theta, wl.n_prefix, rows=rows,
-                          pairing=pairing)
-    dt = time.perf_counter() - t0
+    _CPU_JOB.update(q=inputs.values(q[0]), k=inputs.values(k[0]), v=inputs.values(v[0]), wl=wl,
+                    rows=rows, pairing=pairing)
+    workers = min(cpu_workers(), wl.heads)
+    ctx = mp.get_context("fork")
+    _CPU_JOB["barrier"] = ctx.Barrier(workers)
+    with cf.ProcessPoolExecutor(max_workers=workers, mp_context=ctx) as ex:
+        list(ex.map(_warm_worker, range(workers)))
+        t0 = time.perf_counter()
+        done = sum(ex.map(_oracle_head, range(wl.heads)))
+        dt = time.perf_counter() - t0
+    _CPU_JOB.clear()
+    assert done == rows.size * wl.heads
     flops = 4.0 * rows.size * wl.n_tokens * wl.head_dim * wl.heads
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": workers,
             "kind": "oracle",
             "sample": (f"fp64 oracle, RoPE on Q and K then attention, {rows.size} seeded query "
-                       f"rows x {wl.heads} heads x all {wl.n_tokens} keys of the same workload; "
+                       f"rows x {wl.heads} heads x all {wl.n_tokens} keys of the same workload, "
+                       f"heads spread over {workers} worker processes of one BLAS thread each; "
                        f"{dt:.1f} s wall, {flops / 1e9:.1f} GFLOP"),
             "seconds": dt,
             # the same oracle over every query row, extrapolated linearly in rows
@@ -134,18 +174,26 @@ def main():
     import torch
     from spatiotemporal_attention_vx_amd import binding, configs, inputs
 
-    if not torch.cuda.is_available():
+    # device_count() does not initialise the GPU; the CPU baseline's workers are
+    # forked below, before anything touches it
+    if torch.cuda.device_count() < 1:
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
-    binding.load()
     wl = configs.get(args.workload)
-    dev = torch.device("cuda:0")
-    props = torch.cuda.get_device_properties(dev)
+    pairing = wl.pairing if args.pairing is None else args.pairing
 
-    # ---- inputs: host generation (seeded), one copy to HBM
+    # ---- inputs: host generation (seeded)
     t0 = time.perf_counter()
     q, k, v = inputs.attention_inputs(wl)
     x, sh, sc = inputs.adaln_inputs(wl) if args.adaln == "token" else (None, None, None)
+    gen_s = time.perf_counter() - t0
+    cpu = cpu_baseline(wl, q, k, v, args.cpu_rows, pairing) if args.cpu_rows > 0 else None
+
+    # ---- the GPU from here on; inputs are copied to HBM once
+    binding.load()
+    dev = torch.device("cuda:0")
+    props = torch.cuda.get_device_properties(dev)
+    t0 = time.perf_counter()
 
     def up(a):
         return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
@@ -164,11 +212,7 @@ def main():
         ty = torch.empty(tx.shape, dtype=torch.bfloat16, device=dev)
     adaln_bytes = sum(t.numel() * t.element_size() for t in (tx, tsh, tsc, ty))
     to = torch.empty_like(tq)
-    if args.inputs == "zeros":
-        for t in (tq, tk, tv, tx, tsh, tsc):
-            t.zero_()
-    gen_s = time.perf_counter() - t0
-    pairing = wl.pairing if args.pairing is None else args.pairing
+    gen_s += time.perf_counter() - t0
     desc = binding.RopeDesc.of(wl.grid, wl.split, wl.theta, wl.n_prefix, pairing)
     fused = args.rope == "fused"
     stream = torch.cuda.current_stream()
@@ -257,17 +301,6 @@ def main():
     # and for RoPE's (K read and written in place; a multiply by one keeps the
     # bits), when only K is rotated in the step
     rep_rope_stream = reps(lambda: tk.mul_(1)) if fused else None
-
-    # The bf16 MFMA rate this chip sustains on the same kind of data: a pure
-    # v_mfma loop timed on this GPU right after the step (its clock is set by
-    # the power limit, which depends on the operand data).
-    # It is a reference beside the metric, so a failure here is reported in the
-    # line instead of ending the run.
-    from spatiotemporal_attention_vx_amd import diag
-    try:
-        ceiling = diag.ceiling("zeros" if args.inputs == "zeros" else "normal")
-    except Exception as exc:  # the hot path's own failures are not caught anywhere
-        ceiling = {"error": f"{type(exc).__name__}: {exc}"}
 
     if args.copy_calibration:
         src = torch.empty(1 << 29, dtype=torch.bfloat16, device=dev).normal_()
@@ -364,29 +397,14 @@ def main():
             "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
             "traffic": measured_traffic(wl, args, pairing),
             "kernel": attention_kernel_name(wl),
-            "measured_ceiling": ({
-                "tflops": round(ceiling["tflops"], 1),
-                "frac_of_peak": round(ceiling["tflops"] / PEAK_BF16_TFLOPS, 4),
-                "attn_frac_of_ceiling": round(attn_tflops / ceiling["tflops"], 4),
-                "what": ("pure v_mfma_f32_32x32x16_bf16 loop on "
-                         + ("all-zero" if args.inputs == "zeros" else "N(0,1) bf16")
-                         + f" operands, {ceiling['launch']}, same GPU, same run: the rate the "
-                           "chip's power limit allows on this data"),
-            } if "tflops" in ceiling else None),
-            **({"measured_ceiling_error": ceiling["error"]} if "error" in ceiling else {}),
         },
         "kernels": kernels,
         "device": {"name": props.name, "cus": props.multi_processor_count,
                    "gcn_arch": getattr(props, "gcnArchName", "")},
         "input_setup_s": round(gen_s, 2),
     }
-    if args.inputs == "zeros":
-        record["data"] = "synthetic, every input zero"
-        record["diagnostic"] = ("all-zero inputs: the same launches and instructions with "
-                                "almost no data toggling, to separate the chip's power limit "
-                                "from the kernel's schedule; not the metric's workload")
-    if args.cpu_rows > 0 and args.inputs == "normal":
-        record["cpu_baseline"] = cpu_baseline(wl, q, k, v, args.cpu_rows, pairing)
+    if cpu is not None:
+        record["cpu_baseline"] = cpu
     print(json.dumps(record), flush=True)
 
 

@@ -16,9 +16,6 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libvx.so")
-# measurement aid (not the hot path): the MFMA ceiling probe bench.py times
-DIAG_SRC = os.path.join(PKG, "diag", "mfma_ceiling.hip")
-DIAG_LIB = os.path.join(PKG, "libvx_diag.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 ARCH = "gfx950"
 
@@ -64,19 +61,7 @@ def build(verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
     os.replace(tmp, LIB)
-    build_diag()
     return LIB
-
-
-def build_diag() -> str:
-    """The separate measurement-aid library (one source, no dependency on libvx)."""
-    tmp = DIAG_LIB + ".tmp"
-    r = subprocess.run([hipcc(), *FLAGS, "-shared", DIAG_SRC, "-o", tmp],
-                       capture_output=True, text=True)
-    if r.returncode != 0:
-        raise RuntimeError(f"hipcc failed on {DIAG_SRC}:\n{r.stderr}")
-    os.replace(tmp, DIAG_LIB)
-    return DIAG_LIB
 
 
 if __name__ == "__main__":

@@ -38,7 +38,7 @@ def test_no_gpu_fails_loudly():
 
 def _args(**kw):
     d = dict(gpus=1, steps=10, warmup=3, workload="large", rope="fused", adaln="token",
-             pairing=None, kv_split=0, cpu_rows=512, inputs="normal", copy_calibration=False)
+             pairing=None, kv_split=0, cpu_rows=1024, copy_calibration=False)
     d.update(kw)
     return argparse.Namespace(**d)
 
@@ -59,7 +59,6 @@ def test_traffic_record_only_for_its_own_launch():
     assert bench.measured_traffic(large, _args(kv_split=37811), 0) is None
     assert bench.measured_traffic(large, _args(rope="separate"), 0) is None
     assert bench.measured_traffic(large, _args(), 2) is None
-    assert bench.measured_traffic(large, _args(inputs="zeros"), 0) is None
 
 
 def test_traffic_record_is_consistent():

@@ -35,9 +35,7 @@ def test_one_json_line_with_the_contract_fields(gpu_lib):
     assert rf["bound"] == "mfma" and rf["unit"] == "TFLOP/s" and rf["peak"] == 2500.0
     assert rf["achieved"] > 0 and abs(rf["frac"] - rf["achieved"] / rf["peak"]) < 1e-3
     assert "traffic" in rf and rf["traffic"] is None        # recorded for the large launch only
-    ceil = rf["measured_ceiling"]
-    assert ceil is not None and ceil["tflops"] > 0
-    assert abs(ceil["attn_frac_of_ceiling"] - rf["achieved"] / ceil["tflops"]) < 1e-3
+    assert "measured_ceiling" not in rf
     cb = d["cpu_baseline"]
     assert cb["kind"] == "oracle" and cb["value"] > 0 and cb["cores"] >= 1
     assert isinstance(cb["unit"], str) and "8 seeded query rows" in cb["sample"]
