@@ -89,16 +89,18 @@ typedef struct {
  *   y[n, :] = (x[n, :] - mean_n) / sqrt(var_n + eps) * (1 + scale[n, :]) + shift[n, :]
  *
  * mean_n and the biased variance var_n are taken over the `hidden` values of
- * row n; there is no learnable affine.  x, shift, scale, y: [n_rows, hidden]
- * of type dt.  y == x (in place) is allowed; no other overlap is.
+ * row n; there is no learnable affine.  x, shift, scale, y: [n_tokens,
+ * hidden] of type dt (one row per token).  y == x (in place) is allowed; no
+ * other overlap is.
  * Errors: VX_ERR_NULL (x, shift, scale or y NULL); VX_ERR_INVALID
- * (n_rows < 0, hidden <= 0, eps < 0 or not finite, bad dt);
+ * (n_tokens < 0, hidden <= 0, eps < 0 or not finite, bad dt);
  * VX_ERR_UNSUPPORTED (hidden not a multiple of 8 for bf16 or 4 for f32, or
  * hidden above 8192 for bf16 or 4096 for f32: a row is held in registers);
  * VX_ERR_ALIGN.  n_rows == 0 launches nothing.
  */
-int vx_adaln_modulate(const void* x, const void* shift, const void* scale, void* y,
-                      int64_t n_rows, int64_t hidden, float eps, int dt, void* hip_stream);
+vx_status vx_adaln_modulate(const void* x, const void* shift, const void* scale, void* y,
+                            int64_t n_tokens, int64_t hidden, float eps, vx_dtype dt,
+                            void* hip_stream);
 
 /*
  * AdaLN modulation with per-sample or per-token tables and mixed dtypes
@@ -115,8 +117,8 @@ int vx_adaln_modulate(const void* x, const void* shift, const void* scale, void*
  * LN as for vx_adaln_modulate.  x: [batch, n_tokens, hidden] of x_dt;
  * shift, scale: [batch, mod_tokens, hidden] of mod_dt; y: [batch, n_tokens,
  * hidden] of y_dt.  Each dtype is VX_F32 or VX_BF16 independently; the
- * arithmetic is float32.  vx_adaln_modulate(x, .., n_rows, ..) is this call
- * with batch 1, n_tokens = mod_tokens = n_rows and one dtype throughout.
+ * arithmetic is float32.  vx_adaln_modulate(x, .., n_tokens, ..) is this
+ * call with batch 1, mod_tokens = n_tokens and one dtype throughout.
  * y == x is allowed when x_dt == y_dt; no other overlap with y is.
  * Errors: VX_ERR_NULL; VX_ERR_INVALID (batch or n_tokens < 0, hidden <= 0,
  * mod_tokens neither n_tokens nor 1, eps < 0 or not finite, a bad dtype,
@@ -125,9 +127,10 @@ int vx_adaln_modulate(const void* x, const void* shift, const void* scale, void*
  * of 4 and at most 4096: a row is held in registers); VX_ERR_ALIGN.
  * batch * n_tokens == 0 launches nothing.
  */
-int vx_adaln_modulate_ex(const void* x, const void* shift, const void* scale, void* y,
-                         int64_t batch, int64_t n_tokens, int64_t hidden, int64_t mod_tokens,
-                         float eps, int x_dt, int mod_dt, int y_dt, void* hip_stream);
+vx_status vx_adaln_modulate_ex(const void* x, const void* shift, const void* scale, void* y,
+                               int64_t batch, int64_t n_tokens, int64_t hidden,
+                               int64_t mod_tokens, float eps, vx_dtype x_dt, vx_dtype mod_dt,
+                               vx_dtype y_dt, void* hip_stream);
 
 /*
  * 3D RoPE on Q and K, in place (vidax paper §2 "3D RoPE, 3D VAEs, and flash
@@ -139,8 +142,9 @@ int vx_adaln_modulate_ex(const void* x, const void* shift, const void* scale, vo
  * mis-summed bands, theta <= 0 or not finite, pairing not 0, 1 or 2, q == k);
  * VX_ERR_UNSUPPORTED (head_dim not a multiple of 8, or > 256); VX_ERR_ALIGN.
  */
-int vx_rope3d_apply(void* q, void* k, int64_t batch, int64_t n_tokens, int64_t heads,
-                    int64_t head_dim, const vx_rope3d_desc* rope, int dt, void* hip_stream);
+vx_status vx_rope3d_apply(void* q, void* k, int64_t batch, int64_t n_tokens, int64_t heads,
+                          int64_t head_dim, const vx_rope3d_desc* rope, vx_dtype dt,
+                          void* hip_stream);
 
 /*
  * Full non-causal attention forward (vidax paper §1: full self-attention
@@ -167,10 +171,10 @@ int vx_rope3d_apply(void* q, void* k, int64_t batch, int64_t n_tokens, int64_t h
  * input); VX_ERR_UNSUPPORTED (head_dim not 64 or 128, more than 2^30 tokens, or
  * heads * head_dim above 2^22); VX_ERR_ALIGN.
  */
-int vx_flash_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
-                      int64_t batch, int64_t n_tokens, int64_t heads, int64_t head_dim,
-                      float softmax_scale, const vx_rope3d_desc* rope_q, int dt,
-                      void* hip_stream);
+vx_status vx_flash_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                            int64_t batch, int64_t n_tokens, int64_t heads, int64_t head_dim,
+                            float softmax_scale, const vx_rope3d_desc* rope_q, vx_dtype dt,
+                            void* hip_stream);
 
 /*
  * Attention of n_q queries over a separate set of n_kv keys (and values):
@@ -188,10 +192,10 @@ int vx_flash_attn_fwd(const void* q, const void* k, const void* v, void* o, floa
  * n_tokens.  Errors: as vx_flash_attn_fwd, with n_q <= 0 or n_kv <= 0
  * reported as VX_ERR_INVALID.
  */
-int vx_flash_attn_fwd_kv(const void* q, const void* k, const void* v, void* o, float* lse,
-                         int64_t batch, int64_t n_q, int64_t n_kv, int64_t heads,
-                         int64_t head_dim, float softmax_scale, const vx_rope3d_desc* rope_q,
-                         int dt, void* hip_stream);
+vx_status vx_flash_attn_fwd_kv(const void* q, const void* k, const void* v, void* o, float* lse,
+                               int64_t batch, int64_t n_q, int64_t n_kv, int64_t heads,
+                               int64_t head_dim, float softmax_scale,
+                               const vx_rope3d_desc* rope_q, vx_dtype dt, void* hip_stream);
 
 /*
  * Attention with key padding: as vx_flash_attn_fwd_kv, with keys
@@ -211,10 +215,11 @@ int vx_flash_attn_fwd_kv(const void* q, const void* k, const void* v, void* o, f
  * VX_ERR_INVALID (a range outside 0 <= lo <= hi <= n_kv, or one that
  * leaves no valid key); VX_ERR_UNSUPPORTED (batch > 64).
  */
-int vx_flash_attn_fwd_masked(const void* q, const void* k, const void* v, void* o, float* lse,
-                             int64_t batch, int64_t n_q, int64_t n_kv, int64_t heads,
-                             int64_t head_dim, float softmax_scale, const vx_rope3d_desc* rope_q,
-                             const int32_t* key_pad, int dt, void* hip_stream);
+vx_status vx_flash_attn_fwd_masked(const void* q, const void* k, const void* v, void* o,
+                                   float* lse, int64_t batch, int64_t n_q, int64_t n_kv,
+                                   int64_t heads, int64_t head_dim, float softmax_scale,
+                                   const vx_rope3d_desc* rope_q, const int32_t* key_pad,
+                                   vx_dtype dt, void* hip_stream);
 
 /*
  * Merge of two partial attention results over disjoint key sets A and B
@@ -234,9 +239,10 @@ int vx_flash_attn_fwd_masked(const void* q, const void* k, const void* v, void* 
  * (sizes <= 0, bad dt, overlaps); VX_ERR_UNSUPPORTED (head_dim not 64 or
  * 128); VX_ERR_ALIGN (o tensors not 16-byte, LSEs not 4-byte aligned).
  */
-int vx_attn_merge2(const void* o_a, const float* lse_a, const void* o_b, const float* lse_b,
-                   void* o, float* lse, int64_t batch, int64_t n_tokens, int64_t heads,
-                   int64_t head_dim, int dt, void* hip_stream);
+vx_status vx_attn_merge2(const void* o_a, const float* lse_a, const void* o_b,
+                         const float* lse_b, void* o, float* lse, int64_t batch,
+                         int64_t n_tokens, int64_t heads, int64_t head_dim, vx_dtype dt,
+                         void* hip_stream);
 
 /* Message of the last failed vx_* call on this thread ("" if none). */
 const char* vx_last_error(void);

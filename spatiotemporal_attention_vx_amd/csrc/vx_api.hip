@@ -229,78 +229,35 @@ int flash_attn(const char* fn, const void* q, const void* k, const void* v, void
                     fn);
 }
 
-}  // namespace
-
-extern "C" {
-
-int vx_adaln_modulate(const void* x, const void* shift, const void* scale, void* y,
-                      int64_t n_rows, int64_t hidden, float eps, int dt, void* hip_stream) {
-    return adaln("vx_adaln_modulate", x, shift, scale, y, 1, n_rows, hidden, n_rows, eps, dt, dt,
-                 dt, hip_stream);
-}
-
-int vx_adaln_modulate_ex(const void* x, const void* shift, const void* scale, void* y,
-                         int64_t batch, int64_t n_tokens, int64_t hidden, int64_t mod_tokens,
-                         float eps, int x_dt, int mod_dt, int y_dt, void* hip_stream) {
-    return adaln("vx_adaln_modulate_ex", x, shift, scale, y, batch, n_tokens, hidden, mod_tokens,
-                 eps, x_dt, mod_dt, y_dt, hip_stream);
-}
-
-int vx_rope3d_apply(void* q, void* k, int64_t batch, int64_t n_tokens, int64_t heads,
-                    int64_t head_dim, const vx_rope3d_desc* rope, int dt, void* hip_stream) {
-    if ((!q && !k) || !rope) return fail(VX_ERR_NULL, "vx_rope3d_apply: q and k both NULL, or rope NULL");
-    if (int e = check_dtype("vx_rope3d_apply", dt)) return e;
+int rope3d(const char* fn, void* q, void* k, int64_t batch, int64_t n_tokens, int64_t heads,
+           int64_t head_dim, const vx_rope3d_desc* rope, int dt, void* hip_stream) {
+    if ((!q && !k) || !rope) return fail(VX_ERR_NULL, "%s: q and k both NULL, or rope NULL", fn);
+    if (int e = check_dtype(fn, dt)) return e;
     if (batch <= 0 || n_tokens <= 0 || heads <= 0 || head_dim <= 0)
-        return fail(VX_ERR_INVALID, "vx_rope3d_apply: sizes must be positive");
-    if (q == k) return fail(VX_ERR_INVALID, "vx_rope3d_apply: q and k must differ");
+        return fail(VX_ERR_INVALID, "%s: sizes must be positive", fn);
+    if (q == k) return fail(VX_ERR_INVALID, "%s: q and k must differ", fn);
     if (head_dim % 8 != 0 || head_dim > 256)
-        return fail(VX_ERR_UNSUPPORTED, "vx_rope3d_apply: head_dim %lld must be a multiple of 8 and <= 256",
+        return fail(VX_ERR_UNSUPPORTED, "%s: head_dim %lld must be a multiple of 8 and <= 256", fn,
                     (long long)head_dim);
     vx::RopeArgs r;
-    if (int e = check_rope("vx_rope3d_apply", rope, n_tokens, head_dim, &r)) return e;
+    if (int e = check_rope(fn, rope, n_tokens, head_dim, &r)) return e;
     if ((q && !aligned16(q)) || (k && !aligned16(k)))
-        return fail(VX_ERR_ALIGN, "vx_rope3d_apply: tensors must be 16-byte aligned");
+        return fail(VX_ERR_ALIGN, "%s: tensors must be 16-byte aligned", fn);
     const int64_t esz = dt == VX_BF16 ? 2 : 4;
     int64_t bytes, rows;
     if (!mul_ok(bytes, {batch, n_tokens, heads, head_dim, esz}) || !mul_ok(rows, {batch, n_tokens}) ||
         heads * head_dim / (esz == 2 ? 8 : 4) > INT32_MAX / 4 || (rows + 3) / 4 > INT32_MAX)
-        return fail(VX_ERR_INVALID, "vx_rope3d_apply: size overflow");
+        return fail(VX_ERR_INVALID, "%s: size overflow", fn);
     if (q && k && overlaps(q, bytes, k, bytes))
-        return fail(VX_ERR_INVALID, "vx_rope3d_apply: q and k overlap");
+        return fail(VX_ERR_INVALID, "%s: q and k overlap", fn);
     return launched(vx::launch_rope3d(q, k, batch, n_tokens, heads, head_dim, r, dt == VX_BF16,
                                       (hipStream_t)hip_stream),
-                    "vx_rope3d_apply");
+                    fn);
 }
 
-int vx_flash_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
-                      int64_t batch, int64_t n_tokens, int64_t heads, int64_t head_dim,
-                      float softmax_scale, const vx_rope3d_desc* rope_q, int dt,
-                      void* hip_stream) {
-    return flash_attn("vx_flash_attn_fwd", q, k, v, o, lse, batch, n_tokens, n_tokens, heads,
-                      head_dim, softmax_scale, rope_q, nullptr, dt, hip_stream);
-}
-
-int vx_flash_attn_fwd_kv(const void* q, const void* k, const void* v, void* o, float* lse,
-                         int64_t batch, int64_t n_q, int64_t n_kv, int64_t heads,
-                         int64_t head_dim, float softmax_scale, const vx_rope3d_desc* rope_q,
-                         int dt, void* hip_stream) {
-    return flash_attn("vx_flash_attn_fwd_kv", q, k, v, o, lse, batch, n_q, n_kv, heads, head_dim,
-                      softmax_scale, rope_q, nullptr, dt, hip_stream);
-}
-
-int vx_flash_attn_fwd_masked(const void* q, const void* k, const void* v, void* o, float* lse,
-                             int64_t batch, int64_t n_q, int64_t n_kv, int64_t heads,
-                             int64_t head_dim, float softmax_scale, const vx_rope3d_desc* rope_q,
-                             const int32_t* key_pad, int dt, void* hip_stream) {
-    if (!key_pad) return fail(VX_ERR_NULL, "vx_flash_attn_fwd_masked: key_pad NULL");
-    return flash_attn("vx_flash_attn_fwd_masked", q, k, v, o, lse, batch, n_q, n_kv, heads,
-                      head_dim, softmax_scale, rope_q, key_pad, dt, hip_stream);
-}
-
-int vx_attn_merge2(const void* o_a, const float* lse_a, const void* o_b, const float* lse_b,
-                   void* o, float* lse, int64_t batch, int64_t n_tokens, int64_t heads,
-                   int64_t head_dim, int dt, void* hip_stream) {
-    const char* fn = "vx_attn_merge2";
+int attn_merge2(const char* fn, const void* o_a, const float* lse_a, const void* o_b,
+                const float* lse_b, void* o, float* lse, int64_t batch, int64_t n_tokens,
+                int64_t heads, int64_t head_dim, int dt, void* hip_stream) {
     if (!o_a || !lse_a || !o_b || !lse_b || !o) return fail(VX_ERR_NULL, "%s: NULL tensor", fn);
     if (int e = check_dtype(fn, dt)) return e;
     if (batch <= 0 || n_tokens <= 0 || heads <= 0 || head_dim <= 0)
@@ -334,8 +291,71 @@ int vx_attn_merge2(const void* o_a, const float* lse_a, const void* o_b, const f
                     fn);
 }
 
+// Every entry point returns one of the vx_status codes.
+vx_status st(int code) { return static_cast<vx_status>(code); }
+
+}  // namespace
+
+extern "C" {
+
+vx_status vx_adaln_modulate(const void* x, const void* shift, const void* scale, void* y,
+                            int64_t n_tokens, int64_t hidden, float eps, vx_dtype dt,
+                            void* hip_stream) {
+    return st(adaln("vx_adaln_modulate", x, shift, scale, y, 1, n_tokens, hidden, n_tokens, eps,
+                    dt, dt, dt, hip_stream));
+}
+
+vx_status vx_adaln_modulate_ex(const void* x, const void* shift, const void* scale, void* y,
+                               int64_t batch, int64_t n_tokens, int64_t hidden,
+                               int64_t mod_tokens, float eps, vx_dtype x_dt, vx_dtype mod_dt,
+                               vx_dtype y_dt, void* hip_stream) {
+    return st(adaln("vx_adaln_modulate_ex", x, shift, scale, y, batch, n_tokens, hidden,
+                    mod_tokens, eps, x_dt, mod_dt, y_dt, hip_stream));
+}
+
+vx_status vx_rope3d_apply(void* q, void* k, int64_t batch, int64_t n_tokens, int64_t heads,
+                          int64_t head_dim, const vx_rope3d_desc* rope, vx_dtype dt,
+                          void* hip_stream) {
+    return st(rope3d("vx_rope3d_apply", q, k, batch, n_tokens, heads, head_dim, rope, dt,
+                     hip_stream));
+}
+
+vx_status vx_flash_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                            int64_t batch, int64_t n_tokens, int64_t heads, int64_t head_dim,
+                            float softmax_scale, const vx_rope3d_desc* rope_q, vx_dtype dt,
+                            void* hip_stream) {
+    return st(flash_attn("vx_flash_attn_fwd", q, k, v, o, lse, batch, n_tokens, n_tokens, heads,
+                         head_dim, softmax_scale, rope_q, nullptr, dt, hip_stream));
+}
+
+vx_status vx_flash_attn_fwd_kv(const void* q, const void* k, const void* v, void* o, float* lse,
+                               int64_t batch, int64_t n_q, int64_t n_kv, int64_t heads,
+                               int64_t head_dim, float softmax_scale,
+                               const vx_rope3d_desc* rope_q, vx_dtype dt, void* hip_stream) {
+    return st(flash_attn("vx_flash_attn_fwd_kv", q, k, v, o, lse, batch, n_q, n_kv, heads,
+                         head_dim, softmax_scale, rope_q, nullptr, dt, hip_stream));
+}
+
+vx_status vx_flash_attn_fwd_masked(const void* q, const void* k, const void* v, void* o,
+                                   float* lse, int64_t batch, int64_t n_q, int64_t n_kv,
+                                   int64_t heads, int64_t head_dim, float softmax_scale,
+                                   const vx_rope3d_desc* rope_q, const int32_t* key_pad,
+                                   vx_dtype dt, void* hip_stream) {
+    if (!key_pad) return st(fail(VX_ERR_NULL, "vx_flash_attn_fwd_masked: key_pad NULL"));
+    return st(flash_attn("vx_flash_attn_fwd_masked", q, k, v, o, lse, batch, n_q, n_kv, heads,
+                         head_dim, softmax_scale, rope_q, key_pad, dt, hip_stream));
+}
+
+vx_status vx_attn_merge2(const void* o_a, const float* lse_a, const void* o_b,
+                         const float* lse_b, void* o, float* lse, int64_t batch,
+                         int64_t n_tokens, int64_t heads, int64_t head_dim, vx_dtype dt,
+                         void* hip_stream) {
+    return st(attn_merge2("vx_attn_merge2", o_a, lse_a, o_b, lse_b, o, lse, batch, n_tokens,
+                          heads, head_dim, dt, hip_stream));
+}
+
 const char* vx_last_error(void) { return g_error.c_str(); }
 
-int vx_version(void) { return 200; }
+int vx_version(void) { return 201; }
 
 }  // extern "C"
