@@ -95,7 +95,7 @@ typedef struct {
  * Errors: VX_ERR_NULL (x, shift, scale or y NULL); VX_ERR_INVALID
  * (n_tokens < 0, hidden <= 0, eps < 0 or not finite, bad dt);
  * VX_ERR_UNSUPPORTED (hidden not a multiple of 8 for bf16 or 4 for f32, or
- * hidden above 8192 for bf16 or 4096 for f32: a row is held in registers);
+ * above 8192: a row is held in registers);
  * VX_ERR_ALIGN.  n_rows == 0 launches nothing.
  */
 vx_status vx_adaln_modulate(const void* x, const void* shift, const void* scale, void* y,
@@ -122,9 +122,9 @@ vx_status vx_adaln_modulate(const void* x, const void* shift, const void* scale,
  * y == x is allowed when x_dt == y_dt; no other overlap with y is.
  * Errors: VX_ERR_NULL; VX_ERR_INVALID (batch or n_tokens < 0, hidden <= 0,
  * mod_tokens neither n_tokens nor 1, eps < 0 or not finite, a bad dtype,
- * overlaps, y == x with different dtypes); VX_ERR_UNSUPPORTED (hidden not a
- * multiple of 8 and at most 8192; when all three dtypes are f32, a multiple
- * of 4 and at most 4096: a row is held in registers); VX_ERR_ALIGN.
+ * overlaps, y == x with different dtypes); VX_ERR_UNSUPPORTED (hidden above
+ * 8192, or not a multiple of 8, of 4 when all three dtypes are f32: a row is
+ * held in registers); VX_ERR_ALIGN.
  * batch * n_tokens == 0 launches nothing.
  */
 vx_status vx_adaln_modulate_ex(const void* x, const void* shift, const void* scale, void* y,
@@ -161,11 +161,15 @@ vx_status vx_rope3d_apply(void* q, void* k, int64_t batch, int64_t n_tokens, int
  * registers as it is loaded (its buffer is not modified; the result equals
  * vx_rope3d_apply on Q first); K must already be rotated.  o must not
  * overlap q, k or v.
- * Precision (bf16): scores and sums are fp32, P is rounded to bf16 for the
- * P V product, and q * scale * log2(e) is rounded to bf16 once as Q is
- * loaded.  The LSE therefore moves by up to about 2^-9 of the largest
- * scale * sum_e |q_e k_e| of the row (0.07 at scores near 80); o is not
- * affected beyond its bf16 tolerance, since softmax ignores a common shift.
+ * Precision (bf16): scores, row sums and the accumulator are fp32, and the
+ * softmax weights are rounded to bf16 for the P V product.  When lse is
+ * NULL, q * scale * log2(e) is also rounded to bf16 once as Q is loaded
+ * (one multiply fewer per score); softmax ignores the common shift this
+ * gives a row's scores, so o stays within its bf16 tolerance.  When lse is
+ * given, Q is used exactly as stored and the scale is applied in fp32 before
+ * each exponential, so the LSE carries only fp32 rounding and that of the
+ * bf16 weights (at most 2^-9 relative in the sum).  The two forms may differ
+ * in the last bits of o.
  * Errors: VX_ERR_NULL (q, k, v or o NULL); VX_ERR_INVALID (sizes <= 0,
  * softmax_scale not finite, bad rope_q as for vx_rope3d_apply, o aliasing an
  * input); VX_ERR_UNSUPPORTED (head_dim not 64 or 128, more than 2^30 tokens, or

@@ -262,10 +262,11 @@ template <bool XB, bool MB, bool YB, bool PER_SAMPLE>
 static hipError_t adaln_dispatch_k(const void* x, const void* shift, const void* scale, void* y,
                                    int64_t rows, int64_t n_tokens, int64_t hidden, float eps,
                                    hipStream_t st) {
-    // Rows are held in registers, up to 16 groups per lane: hidden <= 8192
-    // (groups of 8), or <= 4096 when all tensors are f32 (groups of 4).
+    // Rows are held in registers: hidden <= 8192, i.e. up to 16 groups of 8
+    // per lane, or 32 groups of 4 when all tensors are f32 (then only x is
+    // held past 16 groups; the tables are read in the output pass).
     constexpr int G = ada_group<XB, MB, YB>();
-    constexpr int KMAX = 16;
+    constexpr int KMAX = 8192 / 64 / G;
     const int groups = (int)(hidden / G);
     const int k = (groups + 63) / 64;
     const bool full = groups == 64 * k;
@@ -286,6 +287,9 @@ static hipError_t adaln_dispatch_k(const void* x, const void* shift, const void*
             case 10: VX_ADA(10, true); return hipGetLastError();
             case 12: VX_ADA(12, true); return hipGetLastError();
             case 16: VX_ADA(16, true); return hipGetLastError();
+            case 20: VX_ADA(20, true); return hipGetLastError();
+            case 24: VX_ADA(24, true); return hipGetLastError();
+            case 32: VX_ADA(32, true); return hipGetLastError();
             default: break;
         }
     }
@@ -293,7 +297,8 @@ static hipError_t adaln_dispatch_k(const void* x, const void* shift, const void*
     else if (k <= 2) VX_ADA(2, false);
     else if (k <= 4) VX_ADA(4, false);
     else if (k <= 8) VX_ADA(8, false);
-    else VX_ADA(16, false);
+    else if (k <= 16) VX_ADA(16, false);
+    else VX_ADA(32, false);
 #undef VX_ADA
     return hipGetLastError();
 }

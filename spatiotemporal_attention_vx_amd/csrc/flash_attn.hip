@@ -15,10 +15,18 @@
 //     the wave's Q^T fragment stays in VGPRs as the B operand.  In the
 //     accumulator, lane l holds query l % 32 and 16 of the 32 keys, so the
 //     row statistics are per lane plus one exchange with lane l ^ 32.
-//   * Everything is in base-2 units: Q is multiplied by scale * log2(e) as
-//     it is loaded, and the running row maximum m enters each score through
-//     the MFMA's C operand (a register block holding -m), so the MFMA hands
-//     out u - m directly and the softmax weight is a bare v_exp_f32.
+//   * The running row maximum m enters each score through the MFMA's C
+//     operand (a register block holding -m), so the MFMA hands out s - m
+//     with no per-score subtraction.  Without an LSE output, Q is also
+//     multiplied by scale * log2(e) as it is loaded (rounded to bf16 once),
+//     so s is already a base-2 score and the softmax weight is a bare
+//     v_exp_f32.  That rounding moves every score of a row by a little and
+//     the LSE with it (O does not feel it: softmax ignores a common shift),
+//     so when the caller asks for the LSE the kernel keeps Q exactly as
+//     stored, s is the raw dot product, and the weight is
+//     v_exp_f32(c * (s - m)) with c = scale * log2(e) applied in fp32: one
+//     more multiply per score, and an LSE exact up to fp32 and the bf16
+//     rounding of the weights.
 //   * m is raised lazily: only when some row's maximum exceeds it by more
 //     than 2^8 in weight are the accumulator, the row sums and -m updated.
 //     Weights are therefore <= 2^8, and the final division uses the m that
@@ -83,6 +91,7 @@ struct FaArgs {
     int64_t total_tiles;
     float scale;           // softmax scale (natural units)
     float scale_log2;      // scale * log2(e)
+    float lazy_raw;        // FA_LAZY_LOG2 / scale_log2: the lazy threshold in raw dot units
     int use_rope;
     RopeArgs rope;
     // Key padding: keys pad_lo[b] <= j < pad_hi[b] of batch entry b take no
@@ -160,12 +169,12 @@ constexpr float FA_LAZY_LOG2 = 8.0f;
 // Q fragment of one query row as the B operand of S^T = K Q^T: element
 // (ks, e) is column ks * 16 + g * 8 + e.  The row is optionally rotated by
 // the 3D RoPE (rounded to bf16, exactly as vx_rope3d_apply stores it), then
-// multiplied by scale * log2(e) and rounded to bf16.  The lane holds
+// (unless EXACT) multiplied by scale * log2(e) and rounded to bf16.  The lane holds
 // columns g * 8 .. g * 8 + 7 of every 16: with adjacent pairs, or with the
 // head split in halves (column c pairs with c + D/2, which is k-step
 // ks + D/32, same e), both elements of each pair are in the lane; with
 // band halves the partner is read from memory.
-template <int D>
+template <int D, bool EXACT>
 __device__ __forceinline__ void load_q_fragment(const FaArgs& a, const uint16_t* qb, int64_t qi,
                                                 int g, bf16x8_t* qf) {
     constexpr int NKS = D / 16;
@@ -236,9 +245,12 @@ __device__ __forceinline__ void load_q_fragment(const FaArgs& a, const uint16_t*
     }
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
+        if constexpr (!EXACT) {
 #pragma unroll
-        for (int m = 0; m < 4; ++m)
-            u[ks][m] = pack_bf16x2(bf16_lo(u[ks][m]) * a.scale_log2, bf16_hi(u[ks][m]) * a.scale_log2);
+            for (int m = 0; m < 4; ++m)
+                u[ks][m] = pack_bf16x2(bf16_lo(u[ks][m]) * a.scale_log2,
+                                       bf16_hi(u[ks][m]) * a.scale_log2);
+        }
         qf[ks] = __builtin_bit_cast(bf16x8_t, uint4{u[ks][0], u[ks][1], u[ks][2], u[ks][3]});
     }
 }
@@ -282,7 +294,10 @@ __device__ __forceinline__ bf16x4_t lds_read_tr(const lds_u8* p) {
 
 constexpr int FAD_WAVES = 8;
 
-template <int D, bool PAD>
+// EXACT (the caller wants the LSE): Q is kept as stored and scores are raw
+// dot products, scaled by c = scale * log2(e) in fp32 before each
+// exponential; every m and threshold below is in the MFMA's output units.
+template <int D, bool PAD, bool EXACT>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * FAD_WAVES, 64 * FAD_WAVES),
                           amdgpu_waves_per_eu(2, 2)))
 void fa_fwd_bf16_dma_kernel(FaArgs a) {
@@ -318,7 +333,11 @@ void fa_fwd_bf16_dma_kernel(FaArgs a) {
 
     const int64_t qi = (int64_t)qt * BR + wave * 32 + l32;
     bf16x8_t qf[NKK];
-    load_q_fragment<D>(a, a.q + off, qi, g, qf);
+    load_q_fragment<D, EXACT>(a, a.q + off, qi, g, qf);
+    // base-2 exponent of a score in the MFMA's output units
+    const float cw = a.scale_log2;
+    auto weight = [&](float s) { return fast_exp2(EXACT ? s * cw : s); };
+    const float lazy = EXACT ? a.lazy_raw : FA_LAZY_LOG2;
 
     // ---- DMA: instruction m of this wave fills rows RPI I .. RPI I + RPI - 1
     // of the tile, I = wave * NI + m; lane L writes LDS bytes 16 L .. of that
@@ -489,8 +508,8 @@ void fa_fwd_bf16_dma_kernel(FaArgs a) {
             for (int e = 0; e < WPM; ++e) {
                 const int w = i * WPM + e;   // weights 2w, 2w+1: block (2w) / 16 of S(t)
                 const f32x16_t& src = sb[cur((2 * w) / 16)];
-                const float p0 = fast_exp2(src[(2 * w) & 15]);
-                const float p1 = fast_exp2(src[(2 * w + 1) & 15]);
+                const float p0 = weight(src[(2 * w) & 15]);
+                const float p1 = weight(src[(2 * w + 1) & 15]);
                 pw[w] = pack_bf16x2(p0, p1);
             }
             // K(t+3) where K(t) was, one request every NX / NI groups
@@ -554,9 +573,9 @@ void fa_fwd_bf16_dma_kernel(FaArgs a) {
             mx_next = row_max(tm);
         }
         // ---- lazy rescale for S(t+1) (rare after the first tiles)
-        if (t + 1 < nt && __builtin_amdgcn_ballot_w64(mx_next > FA_LAZY_LOG2) != 0) {
+        if (t + 1 < nt && __builtin_amdgcn_ballot_w64(mx_next > lazy) != 0) {
             const float delta = fmaxf(mx_next, 0.f);
-            const float alpha = fast_exp2(-delta);
+            const float alpha = weight(-delta);
             m_ref += delta;
             l_run *= alpha;
 #pragma unroll
@@ -598,7 +617,8 @@ void fa_fwd_bf16_dma_kernel(FaArgs a) {
                 *(uint2*)(ob + db * 32 + 8 * r + 4 * g) = w;
             }
         if (a.lse != nullptr && g == 0)
-            a.lse[bh * nq + qi] = (m_ref + __builtin_log2f(l_tot)) * 0.69314718055994531f;
+            a.lse[bh * nq + qi] =
+                ((EXACT ? m_ref * cw : m_ref) + __builtin_log2f(l_tot)) * 0.69314718055994531f;
     }
 }
 
@@ -745,6 +765,7 @@ hipError_t launch_flash_attn(const void* q, const void* k, const void* v, void* 
     a.dma_max_rows = 0x7fffffff / a.dma_row_bytes;
     a.scale = scale;
     a.scale_log2 = scale * 1.4426950408889634f;
+    a.lazy_raw = FA_LAZY_LOG2 / a.scale_log2;
     a.use_rope = rope != nullptr;
     if (rope) a.rope = *rope;
     else a.rope = RopeArgs{};
@@ -754,15 +775,22 @@ hipError_t launch_flash_attn(const void* q, const void* k, const void* v, void* 
     a.total_tiles = batch * heads * a.n_qtiles;
     const dim3 grid((unsigned)a.total_tiles);
     if (bf16) {
+        // the exact-scale instruction stream only when the LSE is wanted
+        const int code = (head_dim == 128 ? 4 : 0) | (a.has_pad ? 2 : 0) | (lse != nullptr ? 1 : 0);
         const dim3 block(64 * FAD_WAVES);
-        if (head_dim == 128 && a.has_pad)
-            hipLaunchKernelGGL((fa_fwd_bf16_dma_kernel<128, true>), grid, block, 0, st, a);
-        else if (head_dim == 128)
-            hipLaunchKernelGGL((fa_fwd_bf16_dma_kernel<128, false>), grid, block, 0, st, a);
-        else if (a.has_pad)
-            hipLaunchKernelGGL((fa_fwd_bf16_dma_kernel<64, true>), grid, block, 0, st, a);
-        else
-            hipLaunchKernelGGL((fa_fwd_bf16_dma_kernel<64, false>), grid, block, 0, st, a);
+#define VX_FA(C, D, P, E) \
+    case C: hipLaunchKernelGGL((fa_fwd_bf16_dma_kernel<D, P, E>), grid, block, 0, st, a); break;
+        switch (code) {
+            VX_FA(0, 64, false, false)
+            VX_FA(1, 64, false, true)
+            VX_FA(2, 64, true, false)
+            VX_FA(3, 64, true, true)
+            VX_FA(4, 128, false, false)
+            VX_FA(5, 128, false, true)
+            VX_FA(6, 128, true, false)
+            VX_FA(7, 128, true, true)
+        }
+#undef VX_FA
     } else {
         const dim3 block(256);
         if (head_dim == 128) hipLaunchKernelGGL(fa_fwd_f32_kernel<128>, grid, block, 0, st, a);

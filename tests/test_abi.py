@@ -72,7 +72,8 @@ def _rope(**kw):
     ((A, A + MB, A + 2 * MB, A + 3 * MB, 4, 64, 1e-6, 7), INVALID),
     ((A, A + MB, A + 2 * MB, A + 3 * MB, 4, 60, 1e-6, 1), UNSUPPORTED),
     ((A, A + MB, A + 2 * MB, A + 3 * MB, 4, 8200, 1e-6, 1), UNSUPPORTED),
-    ((A, A + MB, A + 2 * MB, A + 3 * MB, 4, 4100, 1e-6, 0), UNSUPPORTED),
+    ((A, A + MB, A + 2 * MB, A + 3 * MB, 4, 8196, 1e-6, 0), UNSUPPORTED),
+    ((A, A + MB, A + 2 * MB, A + 3 * MB, 4, 4102, 1e-6, 0), UNSUPPORTED),
     ((A + 2, A + MB, A + 2 * MB, A + 3 * MB, 4, 64, 1e-6, 1), ALIGN),
     ((A, A + MB, A + 2 * MB, A + 64, 4, 64, 1e-6, 1), INVALID),       # y overlaps x
     ((A, A + MB, A + 2 * MB, A + MB, 4, 64, 1e-6, 1), INVALID),       # y == shift
@@ -93,7 +94,7 @@ def test_adaln_rejects(args, code):
     ((A, A + MB, A + 2 * MB, A), 2, 4, 64, 4, (0, 1, 1), INVALID),               # y == x, dtypes differ
     ((A, A + MB, A + 2 * MB, A + 3 * MB), 2, 4, 12, 4, (0, 1, 0), UNSUPPORTED),  # 12 % 8
     ((A, A + MB, A + 2 * MB, A + 3 * MB), 2, 4, 8200, 4, (0, 1, 1), UNSUPPORTED),
-    ((A, A + MB, A + 2 * MB, A + 3 * MB), 2, 4, 4100, 4, (0, 0, 0), UNSUPPORTED),
+    ((A, A + MB, A + 2 * MB, A + 3 * MB), 2, 4, 8196, 4, (0, 0, 0), UNSUPPORTED),
     ((A, A + MB, A + 2 * MB, A + 3 * MB + 4), 2, 4, 64, 1, (1, 1, 1), ALIGN),
     ((A, A + MB, A + 2 * MB, A + 256), 2, 4, 64, 1, (1, 1, 1), INVALID),         # y overlaps x
 ])

@@ -37,7 +37,7 @@ def test_workload(gpu_lib, name):
 @pytest.mark.parametrize("dtype,rows,hidden", [
     ("bf16", 1, 8), ("bf16", 3, 24), ("bf16", 5, 136), ("bf16", 6, 1000), ("bf16", 9, 3072),
     ("bf16", 2, 8192), ("f32", 1, 4), ("f32", 7, 12), ("f32", 5, 128), ("f32", 3, 1028),
-    ("f32", 2, 4096),
+    ("f32", 2, 4096), ("f32", 3, 4100), ("f32", 2, 5120), ("f32", 5, 6148), ("f32", 3, 8192),
 ])
 def test_ragged(gpu_lib, dtype, rows, hidden):
     say(f"adaln ragged {dtype} rows={rows} hidden={hidden}")

@@ -15,7 +15,7 @@ DTYPES = list(itertools.product(["bf16", "f32"], repeat=3))     # (x, tables, y)
 
 
 def _max_hidden(xd, md, yd):
-    return 4096 if (xd, md, yd) == ("f32", "f32", "f32") else 8192
+    return 8192
 
 
 def _group(xd, md, yd):
@@ -43,6 +43,7 @@ def _ref(x, sh, sc, per_sample, eps=1e-6):
 @pytest.mark.parametrize("per_sample", [False, True])
 @pytest.mark.parametrize("batch,n,hidden", [
     (2, 5, 8), (1, 7, 136), (3, 4, 1000), (2, 3, 5120), (1, 2, 8192), (2, 3, 12), (1, 3, 4096),
+    (2, 3, 4100), (1, 2, 6144),
 ])
 def test_dtype_and_table_layouts(gpu_lib, xd, md, yd, per_sample, batch, n, hidden):
     if hidden % _group(xd, md, yd) or hidden > _max_hidden(xd, md, yd):
@@ -58,7 +59,8 @@ def test_dtype_and_table_layouts(gpu_lib, xd, md, yd, per_sample, batch, n, hidd
 
 
 @pytest.mark.parametrize("dtype,n,hidden", [("bf16", 300, 5120), ("bf16", 41, 1000),
-                                            ("f32", 33, 1028), ("f32", 20, 4096)])
+                                            ("f32", 33, 1028), ("f32", 20, 4096),
+                                            ("f32", 17, 5120), ("f32", 9, 8192)])
 def test_uniform_per_token_equals_vx_adaln_modulate(gpu_lib, dtype, n, hidden):
     import torch
     say(f"adaln_ex == adaln {dtype} n={n} d={hidden}")
@@ -113,3 +115,20 @@ def test_large_workload_variants(gpu_lib, xd, md, per_sample):
     tabs = (sh, sc) if per_sample else (sh[:, rows], sc[:, rows])
     ref = _ref(xs, *tabs, per_sample, wl.eps)[0]
     check(y[rows], ref, "bf16", "adaln_ex large")
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("per_sample", [False, True])
+def test_large_workload_all_f32(gpu_lib, per_sample):
+    """75,600 tokens x 5120 with x, the tables and y all fp32 (a DiT kept in
+    fp32 end to end at the 14B models' width): 5120 = 64 lanes x 20 groups of
+    4, so only x is held in registers and the tables are read in the output
+    pass; the oracle checks 2048 seeded rows."""
+    wl = configs.WORKLOADS["large"]
+    say(f"adaln_ex large all f32 per_sample={per_sample}")
+    x, sh, sc = inputs.adaln_inputs_ex(wl, "f32", "f32", per_sample)
+    y = host(_run(x, sh, sc, "f32", wl.eps))[0]
+    rows = inputs.sample_rows(wl, count=2048)
+    tabs = (sh, sc) if per_sample else (sh[:, rows], sc[:, rows])
+    ref = _ref(x[:, rows], *tabs, per_sample, wl.eps)[0]
+    check(y[rows], ref, "f32", "adaln_ex large all f32")

@@ -18,11 +18,13 @@ def _rand(shape, dtype, seed):
     return inputs.storage(g.standard_normal(shape).astype(np.float32), dtype)
 
 
-def _masked(tq, tk, tv, pads, rope_q=None):
+def _masked(tq, tk, tv, pads, rope_q=None, with_lse=True):
+    """Without the LSE the bf16 kernel runs its other instruction stream
+    (softmax scale folded into Q)."""
     import torch
     b, nq, h, _ = tq.shape
     o = torch.full_like(tq, float("nan"))
-    lse = torch.full((b, h, nq), float("nan"), device="cuda")
+    lse = torch.full((b, h, nq), float("nan"), device="cuda") if with_lse else None
     binding.flash_attn_fwd_masked(tq, tk, tv, o, pads, lse, 0.0, rope_q)
     return o, lse
 
@@ -48,12 +50,14 @@ def test_padded_ranges(gpu_lib, dtype, d, nq, nk, pads):
     k = _rand((batch, nk, 2, d), dtype, seed + 1)
     v = _rand((batch, nk, 2, d), dtype, seed + 2)
     o, lse = _masked(dev(q), dev(k), dev(v), pads)
+    o_fast, _ = _masked(dev(q), dev(k), dev(v), pads, with_lse=False)
     torch.cuda.synchronize()
-    og, lg = host(o), lse.cpu().numpy()
+    og, og_fast, lg = host(o), host(o_fast), lse.cpu().numpy()
     for b, (lo, hi) in enumerate(pads):
         ref, rl = oracle.attention_masked(inputs.values(q[b]), inputs.values(k[b]),
                                           inputs.values(v[b]), lo, hi)
         check(og[b], ref, dtype, f"o[{b}]")
+        check(og_fast[b], ref, dtype, f"o[{b}] (without LSE)")
         assert np.abs(lg[b] - rl).max() <= LSE_TOL[dtype]
 
 
@@ -72,9 +76,13 @@ def test_padded_tail_equals_shorter_key_set(gpu_lib, dtype, d):
     o2 = torch.empty_like(tq)
     l2 = torch.empty_like(l1)
     binding.flash_attn_fwd_kv(tq, tk[:, :ln].contiguous(), tv[:, :ln].contiguous(), o2, l2)
+    o3, _ = _masked(tq, tk, tv, [(ln, nk)], with_lse=False)
+    o4 = torch.empty_like(tq)
+    binding.flash_attn_fwd_kv(tq, tk[:, :ln].contiguous(), tv[:, :ln].contiguous(), o4, None)
     torch.cuda.synchronize()
     np.testing.assert_array_equal(bits(o1), bits(o2))
     np.testing.assert_array_equal(l1.cpu().numpy(), l2.cpu().numpy())
+    np.testing.assert_array_equal(bits(o3), bits(o4))
 
 
 def test_padded_values_are_never_read_into_the_result(gpu_lib):
@@ -108,15 +116,18 @@ def test_joint_text_video_with_padded_text(gpu_lib):
     tq, tk, tv = dev(q), dev(k), dev(v)
     binding.rope3d_apply(None, tk, desc)
     o, lse = _masked(tq, tk, tv, [(lo, hi)], rope_q=desc)
+    o_fast, _ = _masked(tq, tk, tv, [(lo, hi)], rope_q=desc, with_lse=False)
     torch.cuda.synchronize()
     rows = inputs.sample_rows(wl)
     og, lg = host(o)[0, rows], lse.cpu().numpy()[0][:, rows]
-    del o, lse, tq, tk, tv
+    og_fast = host(o_fast)[0, rows]
+    del o, o_fast, lse, tq, tk, tv
     qv, kv, vv = (inputs.values(a[0]) for a in (q, k, v))
     qr = oracle.rope3d_apply(qv[rows], wl.grid, wl.split, wl.theta, wl.n_prefix, tokens=rows)
     kr = oracle.rope3d_apply(kv, wl.grid, wl.split, wl.theta, wl.n_prefix)
     ref, rl = oracle.attention_masked(qr, kr, vv, lo, hi)
     check(og, ref, wl.dtype, "attn masked cogvx15")
+    check(og_fast, ref, wl.dtype, "attn masked cogvx15 (without LSE)")
     lse_err = float(np.abs(lg - rl).max())
     say(f"  lse max abs {lse_err:.3e}")
     assert lse_err <= LSE_TOL[wl.dtype]
