@@ -60,7 +60,7 @@ def parse():
     p.add_argument("--kv-split", type=int, default=0,
                    help="run attention as two key parts [0, S) and [S, N) merged through their "
                         "LSEs (vx_flash_attn_fwd_kv twice + vx_attn_merge2); 0 = one call")
-    p.add_argument("--cpu-rows", type=int, default=1024,
+    p.add_argument("--cpu-rows", type=int, default=8192,
                    help="query rows of the oracle CPU baseline (0 = skip it)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run a plain 1 GiB elementwise copy (HBM counter calibration)")
@@ -96,24 +96,26 @@ def measured_traffic(wl, args, pairing):
 _CPU_JOB = {}
 
 
-def _oracle_head(h):
-    """Worker: the oracle on head h, every sampled query row."""
+def _oracle_head(h, rows=None):
+    """Worker: the oracle on head h, every sampled query row (or `rows`)."""
     import threadpoolctl
     import oracle
     j = _CPU_JOB
     wl = j["wl"]
+    rows = j["rows"] if rows is None else rows
     with threadpoolctl.threadpool_limits(1):
         oracle.attention_rope(j["q"][:, h:h + 1], j["k"][:, h:h + 1], j["v"][:, h:h + 1], wl.grid,
-                              wl.split, wl.theta, wl.n_prefix, rows=j["rows"],
+                              wl.split, wl.theta, wl.n_prefix, rows=rows,
                               pairing=j["pairing"])
-    return j["rows"].size
+    return rows.size
 
 
 def _warm_worker(_):
-    """Untimed: one head's work in a fresh worker (its first call pays the page
-    faults of every buffer size the oracle allocates), then wait until every
-    worker holds one of these tasks, so that each worker takes exactly one."""
-    _oracle_head(0)
+    """Untimed: head 0 on the first 512 sampled rows (the oracle's row block,
+    so every buffer size it allocates) in a fresh worker, which pays the page
+    faults of its first calls; then wait until every worker holds one of these
+    tasks, so that each worker takes exactly one."""
+    _oracle_head(0, _CPU_JOB["rows"][:512])
     _CPU_JOB["barrier"].wait(timeout=600)
     return 0
 

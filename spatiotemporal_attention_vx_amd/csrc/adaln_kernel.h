@@ -149,9 +149,20 @@ __device__ __forceinline__ void wave_merge_equal(float& mean, float& m2, float n
     swap_merge<32>(mean, m2, 32.f * n);
 }
 
+// Waves per row: 2 for f32 tables on a row of 8 or more groups per lane
+// (an even number, every lane full), else 1.  Such a row held by one wave
+// takes 128-256 registers of data per lane, which either costs occupancy or
+// makes the compiler sink the table loads into the output pass; split over
+// two waves, each holds half the row with every load issued up front, and
+// the two half-row summaries are merged through LDS.
+template <bool MB, int K, bool FULL>
+constexpr int ada_split() { return (!MB && FULL && K >= 8 && K % 2 == 0) ? 2 : 1; }
+
 // XB, MB, YB: x, the tables (shift and scale) and y are bf16 (else f32).
 // PER_SAMPLE: the table row of row r is r / n_tokens (else r).  K = groups
 // per lane (row width <= 64 G K).  FULL: every lane holds exactly K groups.
+// A workgroup of four waves takes 4 / S rows (S = ada_split); with S = 2
+// wave w holds groups lane + 64 j, j in [(w & 1) K / 2, (w & 1) K / 2 + K / 2).
 template <bool XB, bool MB, bool YB, bool PER_SAMPLE, int K, bool FULL>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256)))
 void adaln_kernel(const u32x4_t* x, const u32x4_t* __restrict__ shift,
@@ -159,23 +170,30 @@ void adaln_kernel(const u32x4_t* x, const u32x4_t* __restrict__ shift,
                   int groups, int hidden, float eps) {
     constexpr int G = ada_group<XB, MB, YB>();
     constexpr int XC = Grp<XB, G>::C, MC = Grp<MB, G>::C, YC = Grp<YB, G>::C;   // chunks per group
-    const int lane = threadIdx.x & 63;
-    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (row >= rows) return;
+    constexpr int S = ada_split<MB, K, FULL>();
+    constexpr int KW = K / S;                      // groups per lane of this wave
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t row = (int64_t)blockIdx.x * (4 / S) + wave / S;
+    const int j0 = (wave % S) * KW;                // this wave's first group index j
+    // With two waves per row both take part in the LDS exchange below, so a
+    // wave past the last row stays (it loads and stores nothing); a lone wave
+    // past the last row leaves.
+    const bool live = row < rows;
+    if (S == 1 && !live) return;
     const int64_t mrow = PER_SAMPLE ? row / n_tokens : row;
     const u32x4_t* xr = x + row * groups * XC;
     const u32x4_t* shr = shift + mrow * groups * MC;
     const u32x4_t* scr = scale + mrow * groups * MC;
     u32x4_t* yr = y + row * groups * YC;
-    auto valid = [&](int j) { return FULL || lane + 64 * j < groups; };
+    auto valid = [&](int j) { return live && (FULL || lane + 64 * (j0 + j) < groups); };
 
     // Tables are loaded with x unless that would not fit in registers.
-    constexpr bool DEFER = K * 4 * (XC + 2 * MC) > 200;
-    Grp<XB, G> xv[K];
-    Grp<MB, G> sh[DEFER ? 1 : K], sc[DEFER ? 1 : K];
+    constexpr bool DEFER = KW * 4 * (XC + 2 * MC) > 200;
+    Grp<XB, G> xv[KW];
+    Grp<MB, G> sh[DEFER ? 1 : KW], sc[DEFER ? 1 : KW];
 #pragma unroll
-    for (int j = 0; j < K; ++j) {
-        const int g = lane + 64 * j;
+    for (int j = 0; j < KW; ++j) {
+        const int g = lane + 64 * (j0 + j);
         if (valid(j)) {
             xv[j] = load_grp<XB, G, true>(xr, g);
             if constexpr (!DEFER) {
@@ -190,7 +208,7 @@ void adaln_kernel(const u32x4_t* x, const u32x4_t* __restrict__ shift,
     // count is G (j + 1): the merge weights are compile-time constants.
     float mean = 0.f, m2 = 0.f, n = 0.f;
 #pragma unroll
-    for (int j = 0; j < K; ++j) {
+    for (int j = 0; j < KW; ++j) {
         if (valid(j)) {
             float f[G], mj, qj;
             unpack_grp<XB, G>(xv[j], f);
@@ -209,9 +227,21 @@ void adaln_kernel(const u32x4_t* x, const u32x4_t* __restrict__ shift,
         }
     }
 
-    // Wave merge: every lane ends with the row summary.
+    // Wave merge: every lane ends with the row summary (with two waves per
+    // row, that of the wave's half; the halves are then merged through LDS
+    // with the symmetric equal-count form, so both waves get the same bits).
     if constexpr (FULL) {
-        wave_merge_equal(mean, m2, (float)(K * G));
+        wave_merge_equal(mean, m2, (float)(KW * G));
+        if constexpr (S == 2) {
+            __shared__ float half_stats[4][2];
+            if (lane == 0) {
+                half_stats[wave][0] = mean;
+                half_stats[wave][1] = m2;
+            }
+            __syncthreads();
+            chan_merge_equal(mean, m2, half_stats[wave ^ 1][0], half_stats[wave ^ 1][1],
+                             (float)(64 * KW * G));
+        }
     } else {
 #pragma unroll
         for (int off = 32; off >= 1; off >>= 1) {
@@ -225,13 +255,13 @@ void adaln_kernel(const u32x4_t* x, const u32x4_t* __restrict__ shift,
     const float rstd = 1.0f / __builtin_sqrtf(var + eps);
 
 #pragma unroll
-    for (int j = 0; j < K; ++j) {
+    for (int j = 0; j < KW; ++j) {
         if (valid(j)) {
             float fx[G], fs[G], fc[G], out[G];
             unpack_grp<XB, G>(xv[j], fx);
             if constexpr (DEFER) {
-                unpack_grp<MB, G>(load_grp<MB, G, !PER_SAMPLE>(shr, lane + 64 * j), fs);
-                unpack_grp<MB, G>(load_grp<MB, G, !PER_SAMPLE>(scr, lane + 64 * j), fc);
+                unpack_grp<MB, G>(load_grp<MB, G, !PER_SAMPLE>(shr, lane + 64 * (j0 + j)), fs);
+                unpack_grp<MB, G>(load_grp<MB, G, !PER_SAMPLE>(scr, lane + 64 * (j0 + j)), fc);
             } else {
                 unpack_grp<MB, G>(sh[j], fs);
                 unpack_grp<MB, G>(sc[j], fc);
@@ -241,7 +271,7 @@ void adaln_kernel(const u32x4_t* x, const u32x4_t* __restrict__ shift,
                 const float nrm = (fx[e] - mean) * rstd;
                 out[e] = __builtin_fmaf(nrm, 1.0f + fc[e], fs[e]);
             }
-            store_grp<YB, G>(yr, lane + 64 * j, out);
+            store_grp<YB, G>(yr, lane + 64 * (j0 + j), out);
         }
     }
 }
@@ -252,7 +282,8 @@ void adaln_kernel(const u32x4_t* x, const u32x4_t* __restrict__ shift,
 template <bool XB, bool MB, bool YB, bool PER_SAMPLE, int K, bool FULL>
 static void adaln_go(const void* x, const void* shift, const void* scale, void* y, int64_t rows,
                      int64_t n_tokens, int groups, int hidden, float eps, hipStream_t st) {
-    const int64_t blocks = (rows + 3) / 4;
+    constexpr int rows_per_block = 4 / ada_split<MB, K, FULL>();
+    const int64_t blocks = (rows + rows_per_block - 1) / rows_per_block;
     hipLaunchKernelGGL((adaln_kernel<XB, MB, YB, PER_SAMPLE, K, FULL>), dim3((unsigned)blocks),
                        dim3(256), 0, st, (const u32x4_t*)x, (const u32x4_t*)shift,
                        (const u32x4_t*)scale, (u32x4_t*)y, rows, n_tokens, groups, hidden, eps);

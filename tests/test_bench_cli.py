@@ -38,7 +38,7 @@ def test_no_gpu_fails_loudly():
 
 def _args(**kw):
     d = dict(gpus=1, steps=10, warmup=3, workload="large", rope="fused", adaln="token",
-             pairing=None, kv_split=0, cpu_rows=1024, copy_calibration=False)
+             pairing=None, kv_split=0, cpu_rows=8192, copy_calibration=False)
     d.update(kw)
     return argparse.Namespace(**d)
 

@@ -37,6 +37,31 @@ def test_workload(gpu_lib, name):
                                       q[0, :wl.n_prefix].view(np.int16))
 
 
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", ["large_sp8", "mixed_sp4"])
+def test_sp_share_workload(gpu_lib, name):
+    """One GPU's share under sequence parallelism: all 75,600 (85,906) tokens
+    with 5 (12) heads, so a token row is narrow and a workgroup spans 32
+    tokens; every token of Q and K against the oracle."""
+    import torch
+    wl = configs.SP_WORKLOADS[name]
+    say(f"rope sp share {name}: N={wl.n_tokens} H={wl.heads} d={wl.head_dim}")
+    q, k, _ = inputs.attention_inputs(wl)
+    tq, tk = dev(q), dev(k)
+    desc = binding.RopeDesc.of(wl.grid, wl.split, wl.theta, wl.n_prefix)
+    binding.rope3d_apply(tq, tk, desc)
+    torch.cuda.synchronize()
+    for src, t, nm in ((q, tq, "q"), (k, tk, "k")):
+        got_all = host(t)[0]
+        acc = ChunkCheck(wl.dtype, f"rope {name} {nm}")
+        for r0 in range(0, wl.n_tokens, 8192):
+            rows = np.arange(r0, min(r0 + 8192, wl.n_tokens))
+            x = inputs.values(src[0, rows]).astype(np.float64)
+            acc.add(got_all[rows], oracle.rope3d_apply(x, wl.grid, wl.split, wl.theta,
+                                                       wl.n_prefix, tokens=rows))
+        acc.done()
+
+
 @pytest.mark.parametrize("dtype,grid,prefix,heads,d,batch,split", [
     ("f32", (1, 1, 1), 0, 1, 64, 1, (16, 24, 24)),
     ("f32", (2, 3, 5), 7, 3, 128, 2, (44, 42, 42)),
