@@ -31,6 +31,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3        # MI355X dense fp32 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 MALL_BYTES = 256 * 2**20       # MI355X memory-side (Infinity) cache
 METRIC = "flash-attn TFLOP/s + % bf16 MFMA peak at 75,600 tokens, 40 heads × d128"
@@ -51,6 +52,10 @@ def parse():
     p.add_argument("--steps", type=int, default=10)
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--workload", default="large")
+    p.add_argument("--dtype", choices=["workload", "f32"], default="workload",
+                   help="workload: the workload's own storage type (bf16 except tiny); f32: the "
+                        "same shapes with Q, K, V, x and the tables in fp32 (fp32 MFMA "
+                        "attention, rated against the fp32 MFMA peak)")
     p.add_argument("--rope", choices=["fused", "separate"], default="fused",
                    help="fused: K rotated by vx_rope3d_apply, Q inside the attention load")
     p.add_argument("--adaln", choices=list(ADALN_MODES), default="token",
@@ -69,8 +74,8 @@ def parse():
 
 def attention_kernel_name(wl):
     if wl.dtype != "bf16":
-        return f"fa_fwd_f32_kernel<{wl.head_dim}>"
-    return f"fa_fwd_bf16_dma_kernel<{wl.head_dim}, false>"
+        return f"fa_fwd_f32_mfma_kernel<{wl.head_dim}, false>"
+    return f"fa_fwd_bf16_dma_kernel<{wl.head_dim}, false, false>"
 
 
 def measured_traffic(wl, args, pairing):
@@ -80,8 +85,8 @@ def measured_traffic(wl, args, pairing):
     rotated on load, adjacent RoPE pairs) or the kernel source has changed since."""
     import hashlib
     path = os.path.join(ROOT, "profiles", "attention_large_traffic.json")
-    if (wl.name != "large" or args.kv_split or args.rope != "fused" or pairing != 0
-            or not os.path.exists(path)):
+    if (wl.name != "large" or wl.dtype != "bf16" or args.kv_split or args.rope != "fused"
+            or pairing != 0 or not os.path.exists(path)):
         return None
     with open(path) as f:
         rec = json.load(f)
@@ -182,6 +187,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     wl = configs.get(args.workload)
+    if args.dtype == "f32" and wl.dtype != "f32":
+        import dataclasses
+        wl = dataclasses.replace(wl, dtype="f32")
     pairing = wl.pairing if args.pairing is None else args.pairing
 
     # ---- inputs: host generation (seeded)
@@ -203,10 +211,10 @@ def main():
     def up_any(a):
         return up(a) if a.dtype == np.uint16 else torch.from_numpy(a).to(dev)
 
-    tq, tk, tv = up(q), up(k), up(v)
+    tq, tk, tv = up_any(q), up_any(k), up_any(v)
     x_dt, m_dt, per_sample = ADALN_MODES[args.adaln]
     if args.adaln == "token":
-        tx, tsh, tsc = up(x), up(sh), up(sc)
+        tx, tsh, tsc = up_any(x), up_any(sh), up_any(sc)
         ty = torch.empty_like(tx)
     else:
         x, sh, sc = inputs.adaln_inputs_ex(wl, x_dt, m_dt, per_sample)
@@ -364,9 +372,11 @@ def main():
             "merge_gbs": round(merge_bytes / (ms["merge"] * 1e-3) / 1e9, 1),
             "merge_hbm_frac": round(merge_bytes / (ms["merge"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
         })
+    peak = PEAK_F32_TFLOPS if wl.dtype == "f32" else PEAK_BF16_TFLOPS
     record = {
-        "metric": METRIC if wl.name == configs.BENCH_WORKLOAD else
-        (f"flash-attn TFLOP/s + % bf16 MFMA peak at {wl.n_tokens:,} tokens, "
+        "metric": METRIC if wl.name == configs.BENCH_WORKLOAD and wl.dtype == "bf16" else
+        (f"flash-attn TFLOP/s + % {'fp32' if wl.dtype == 'f32' else 'bf16'} MFMA peak at "
+         f"{wl.n_tokens:,} tokens, "
          f"{wl.heads} heads × d{wl.head_dim}"),
         "value": round(value, 2),
         "unit": "TFLOP/s",
@@ -377,7 +387,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": wl.dtype,
         "data": "synthetic",
         "config": {
             "workload": (f"{wl.name}: {wl.grid[0]}x{wl.grid[1]}x{wl.grid[2]} latent grid"
@@ -394,9 +404,9 @@ def main():
         "roofline": {
             "bound": "mfma",
             "achieved": round(attn_tflops, 2),
-            "peak": PEAK_BF16_TFLOPS,
+            "peak": peak,
             "unit": "TFLOP/s",
-            "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
+            "frac": round(attn_tflops / peak, 4),
             "traffic": measured_traffic(wl, args, pairing),
             "kernel": attention_kernel_name(wl),
         },

@@ -61,8 +61,9 @@
 //   * Workgroups are remapped so each XCD works through a contiguous range
 //     of (batch, head, query tile), keeping that head's K/V hot in its L2.
 //
-// f32 path (small problems and parity): a plain VALU kernel, a few lanes per
-// query, K/V tiles staged through LDS, exact expf online softmax.
+// f32 path: fp32 MFMA (v_mfma_f32_32x32x2_f32) for both products with the
+// same transposed-score layout, K/V tiles staged through LDS, fp32 online
+// softmax (described with the kernel below).
 #include <type_traits>
 
 #include "vx_device.h"
@@ -622,112 +623,207 @@ void fa_fwd_bf16_dma_kernel(FaArgs a) {
     }
 }
 
-// ---------------------------------------------------------------- f32 VALU
+// ---------------------------------------------------------------- f32 MFMA
+//
+// fp32 inputs and outputs (a DiT kept in fp32 end to end), fp32 products
+// and sums throughout: v_mfma_f32_32x32x2_f32 for both products.  A
+// workgroup of 4 waves owns 128 query rows of one (batch, head); each wave
+// owns 32.  Lane l = (c, h) with c = l % 32, h = l / 32.
+//   * S^T (32 keys x 32 queries) = K_tile Q^T over D / 2 k-steps; k-step s
+//     takes head-dim column h * D/2 + s in lane half h, so a lane's Q^T
+//     fragment is one contiguous half of its query row (in registers) and
+//     its K operand for four k-steps is one 16-byte LDS read.  The
+//     accumulator holds query c and keys 8 (i / 4) + 4 h + i % 4 (i < 16).
+//   * Online softmax in fp32 on raw dot products: row max over the lane's 16
+//     keys and its partner lane (l ^ 32); weights exp2((s - m) * scale *
+//     log2 e); a row with no valid key yet keeps zero weight.
+//   * O^T (D x 32 queries) += V^T P^T: P^T is the score accumulator itself,
+//     register i being the B operand of the k-step over keys 8 (i / 4) + i % 4
+//     (half 0) and 8 (i / 4) + 4 + i % 4 (half 1); the A operand is V at
+//     those keys read from LDS, so P never moves.
+//   * K and V tiles of 32 keys are staged in LDS (rows padded by 16 bytes),
+//     double-buffered: the next tile's global loads are issued into
+//     registers before the current tile's products and stored to the other
+//     buffer after them, one barrier per tile.  Keys past the end load as
+//     zeros and, like padded keys, get -inf scores.
+constexpr int FA32_WAVES = 4;
+constexpr int FA32_BC = 32;    // keys per tile
 
-constexpr int FA32_BC = 32;
+template <int D, bool PAD>
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * FA32_WAVES, 64 * FA32_WAVES),
+                          amdgpu_waves_per_eu(2, 2)))
+void fa_fwd_f32_mfma_kernel(FaArgs a) {
+    constexpr int HALF = D / 2;                     // head-dim columns of a lane half
+    constexpr int NDB = D / 32;                     // 32-row blocks of O^T
+    constexpr int LROW = D + 4;                     // LDS row stride, floats
+    constexpr int TILE = FA32_BC * LROW;            // floats per staged tile
+    constexpr int F4ROW = D / 4;                    // float4 per tile row
+    constexpr int NF4 = FA32_BC * F4ROW / (64 * FA32_WAVES);   // float4 per thread per tensor
+    static_assert(NF4 * 64 * FA32_WAVES == FA32_BC * F4ROW, "tile rows split evenly");
+    __shared__ __attribute__((aligned(16))) float lds[2 * 2 * TILE];   // [buffer][K, V]
 
-template <int D>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256)))
-void fa_fwd_f32_kernel(FaArgs a) {
-    // Every fused multiply-add below is spelled out; implicit contraction is
-    // off so each score is rounded once and the same value feeds the running
-    // max and the exponent (a lone key then weighs exactly 1).
-#pragma clang fp contract(off)
-    constexpr int TPQ = D / 32;        // lanes per query, 32 elements each
-    constexpr int QPB = 256 / TPQ;     // queries per workgroup
-    __shared__ __attribute__((aligned(16))) float ks[FA32_BC * D];
-    __shared__ __attribute__((aligned(16))) float vs[FA32_BC * D];
-
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, c = lane & 31, h = lane >> 5;
     const int64_t tile = xcd_remap(blockIdx.x, a.total_tiles);
     const int qt = (int)(tile % a.n_qtiles);
     const int64_t bh = tile / a.n_qtiles;
-    const int h = (int)(bh % a.heads);
+    const int hd = (int)(bh % a.heads);
     const int64_t b = bh / a.heads;
-    const int64_t off = b * a.batch_stride + (int64_t)h * D;
-    const int64_t kv_off = b * a.kv_batch_stride + (int64_t)h * D;
-    const float* qb = (const float*)a.q + off;
-    const float* kbp = (const float*)a.k + kv_off;
-    const float* vbp = (const float*)a.v + kv_off;
-    const int64_t nq = a.nq, nk = a.nk;
-    const int64_t plo = a.has_pad ? a.pad_lo[b] : 0, phi = a.has_pad ? a.pad_hi[b] : 0;
+    const float* qb = (const float*)a.q + b * a.batch_stride + (int64_t)hd * D;
+    const float* kb = (const float*)a.k + b * a.kv_batch_stride + (int64_t)hd * D;
+    const float* vb = (const float*)a.v + b * a.kv_batch_stride + (int64_t)hd * D;
+    const int64_t nq = a.nq;
+    const int nk = (int)a.nk;
+    const FaTiles<PAD, FA32_BC> tl(a, b);
+    const int nt = tl.nt;
 
-    const int part = tid % TPQ;
-    const int64_t qi = (int64_t)qt * QPB + tid / TPQ;
-    float qv[32], acc[32];
+    // ---- Q^T fragment: columns h * HALF .. h * HALF + HALF - 1 of query qi,
+    // rotated by the 3D RoPE if asked (the same expressions as
+    // vx_rope3d_apply, so fused and separate rotation agree bit for bit)
+    const int64_t qi = (int64_t)qt * (32 * FA32_WAVES) + wave * 32 + c;
+    float qf[HALF];
+    {
+        const float* qrow = qb + qi * a.row_stride + h * HALF;
 #pragma unroll
-    for (int e = 0; e < 32; ++e) {
-        qv[e] = qi < nq ? qb[qi * a.row_stride + part * 32 + e] : 0.f;
-        acc[e] = 0.f;
-    }
-    int tp = 0, hp = 0, wp = 0;
-    const bool rot = a.use_rope && qi < nq && rope_token_pos(a.rope, qi, &tp, &hp, &wp);
-    if (rot && a.rope.pairing == 0) {
-#pragma unroll
-        for (int m = 0; m < 16; ++m) {
-            const int pair = part * 16 + m;
-            float c, s;
-            rope_cos_sin(a.rope, rope_pair_pos(a.rope, pair, tp, hp, wp), pair, &c, &s);
-            rope_rotate(qv[2 * m], qv[2 * m + 1], c, s);
+        for (int u = 0; u < HALF; u += 4) {
+            float4 w = {0.f, 0.f, 0.f, 0.f};
+            if (qi < nq) w = *(const float4*)(qrow + u);
+            qf[u] = w.x; qf[u + 1] = w.y; qf[u + 2] = w.z; qf[u + 3] = w.w;
         }
-    } else if (rot) {
-        // half-split pairings: partners are read from the row in memory
-        const float* qrow = qb + qi * a.row_stride;
-        float out[32];
+        int tp = 0, hp = 0, wp = 0;
+        const bool rot = a.use_rope && qi < nq && rope_token_pos(a.rope, qi, &tp, &hp, &wp);
+        if (rot && a.rope.pairing == 0) {
 #pragma unroll
-        for (int e = 0; e < 32; ++e) {
-            int pair, partner;
-            bool second;
-            rope_elem_pair(a.rope, part * 32 + e, &pair, &partner, &second);
-            float c, s;
-            rope_cos_sin(a.rope, rope_pair_pos(a.rope, pair, tp, hp, wp), pair, &c, &s);
-            out[e] = rope_rotate_elem(qv[e], qrow[partner], second, c, s);
-        }
-#pragma unroll
-        for (int e = 0; e < 32; ++e) qv[e] = out[e];
-    }
-
-    float m_run = -__builtin_inff(), l_run = 0.f;
-    for (int64_t kv0 = 0; kv0 < nk; kv0 += FA32_BC) {
-        __syncthreads();
-        for (int i = tid; i < FA32_BC * D / 4; i += 256) {
-            const int key = i / (D / 4), col = i % (D / 4);
-            const int64_t kk = kv0 + key;
-            float4 kv = {0.f, 0.f, 0.f, 0.f}, vv = {0.f, 0.f, 0.f, 0.f};
-            if (kk < nk) {
-                kv = *(const float4*)(kbp + kk * a.row_stride + col * 4);
-                vv = *(const float4*)(vbp + kk * a.row_stride + col * 4);
+            for (int m = 0; m < HALF / 2; ++m) {
+                const int pair = h * (HALF / 2) + m;
+                float cv, sv;
+                rope_cos_sin(a.rope, rope_pair_pos(a.rope, pair, tp, hp, wp), pair, &cv, &sv);
+                rope_rotate(qf[2 * m], qf[2 * m + 1], cv, sv);
             }
-            *(float4*)(ks + key * D + col * 4) = kv;
-            *(float4*)(vs + key * D + col * 4) = vv;
-        }
-        __syncthreads();
-        const int cnt = (int)((nk - kv0) < FA32_BC ? (nk - kv0) : FA32_BC);
-        for (int j = 0; j < cnt; ++j) {
-            if (kv0 + j >= plo && kv0 + j < phi) continue;   // padded key
-            const float* kr = ks + j * D + part * 32;
-            float s = 0.f;
+        } else if (rot) {
+            // half-split pairings: partners are read from the row in memory
+            const float* full = qb + qi * a.row_stride;
+            float out[HALF];
 #pragma unroll
-            for (int e = 0; e < 32; ++e) s = __builtin_fmaf(qv[e], kr[e], s);
+            for (int e = 0; e < HALF; ++e) {
+                int pair, partner;
+                bool second;
+                rope_elem_pair(a.rope, h * HALF + e, &pair, &partner, &second);
+                float cv, sv;
+                rope_cos_sin(a.rope, rope_pair_pos(a.rope, pair, tp, hp, wp), pair, &cv, &sv);
+                out[e] = rope_rotate_elem(qf[e], full[partner], second, cv, sv);
+            }
 #pragma unroll
-            for (int x = 1; x < TPQ; x <<= 1) s += __shfl_xor(s, x, 64);
-            s *= a.scale;
-            const float m_new = fmaxf(m_run, s);
-            const float corr = expf(m_run - m_new);
-            const float p = expf(s - m_new);
-            l_run = __builtin_fmaf(l_run, corr, p);
-            const float* vr = vs + j * D + part * 32;
-#pragma unroll
-            for (int e = 0; e < 32; ++e) acc[e] = __builtin_fmaf(acc[e], corr, p * vr[e]);
-            m_run = m_new;
+            for (int e = 0; e < HALF; ++e) qf[e] = out[e];
         }
     }
-    if (qi < nq) {
-        float* ob = (float*)a.o + off + qi * a.row_stride + part * 32;
-        const float inv = 1.0f / l_run;
+
+    // ---- tile staging: float4 f = tid + 256 j of a tile is row f / F4ROW,
+    // columns 4 (f % F4ROW) ..; rows past the key count load as zeros
+    float4 rk[NF4], rv[NF4];
+    auto stage_load = [&](int t) {
+        const int kv0 = t * FA32_BC;
 #pragma unroll
-        for (int e = 0; e < 32; ++e) ob[e] = acc[e] * inv;
-        if (a.lse != nullptr && part == 0) a.lse[bh * nq + qi] = m_run + logf(l_run);
+        for (int j = 0; j < NF4; ++j) {
+            const int f = tid + 64 * FA32_WAVES * j, row = f / F4ROW, col = f % F4ROW;
+            const int key = kv0 + row;
+            rk[j] = rv[j] = float4{0.f, 0.f, 0.f, 0.f};
+            if (key < nk) {
+                rk[j] = *(const float4*)(kb + (int64_t)key * a.row_stride + col * 4);
+                rv[j] = *(const float4*)(vb + (int64_t)key * a.row_stride + col * 4);
+            }
+        }
+    };
+    auto stage_store = [&](int buf) {
+#pragma unroll
+        for (int j = 0; j < NF4; ++j) {
+            const int f = tid + 64 * FA32_WAVES * j, row = f / F4ROW, col = f % F4ROW;
+            *(float4*)(lds + (2 * buf) * TILE + row * LROW + col * 4) = rk[j];
+            *(float4*)(lds + (2 * buf + 1) * TILE + row * LROW + col * 4) = rv[j];
+        }
+    };
+    stage_load(0);
+    stage_store(0);
+    __syncthreads();
+
+    const float cl = a.scale_log2;      // scale * log2(e)
+    f32x16_t o[NDB];
+#pragma unroll
+    for (int j = 0; j < NDB; ++j) o[j] = f32x16_t{};
+    float m_run = -__builtin_inff(), l_run = 0.f;
+
+    for (int t = 0; t < nt; ++t) {
+        const int buf = t & 1;
+        const float* kt = lds + (2 * buf) * TILE;
+        const float* vt = lds + (2 * buf + 1) * TILE;
+
+        // S^T = K Q^T
+        f32x16_t s = f32x16_t{};
+#pragma unroll
+        for (int u = 0; u < HALF; u += 4) {
+            const float4 k4 = *(const float4*)(kt + c * LROW + h * HALF + u);
+            s = __builtin_amdgcn_mfma_f32_32x32x2f32(k4.x, qf[u], s, 0, 0, 0);
+            s = __builtin_amdgcn_mfma_f32_32x32x2f32(k4.y, qf[u + 1], s, 0, 0, 0);
+            s = __builtin_amdgcn_mfma_f32_32x32x2f32(k4.z, qf[u + 2], s, 0, 0, 0);
+            s = __builtin_amdgcn_mfma_f32_32x32x2f32(k4.w, qf[u + 3], s, 0, 0, 0);
+            if ((u & 15) == 12) __builtin_amdgcn_sched_barrier(0);
+        }
+        // the next tile's loads, in flight under the softmax and P V
+        if (t + 1 < nt) stage_load(t + 1);
+        if (tl.masked(t)) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                if (tl.dead(t * FA32_BC + 8 * (i >> 2) + 4 * h + (i & 3))) s[i] = -__builtin_inff();
+        }
+
+        // online softmax (raw dot units; -inf stands for "no valid key yet")
+        float mx = s[0];
+#pragma unroll
+        for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[i]);
+        const float m_new = fmaxf(m_run, half_max(mx));
+        const float m_use = m_new == -__builtin_inff() ? 0.f : m_new;
+        const float alpha = __builtin_amdgcn_exp2f((m_run - m_use) * cl);
+        float ps = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            s[i] = __builtin_amdgcn_exp2f((s[i] - m_use) * cl);
+            ps += s[i];
+        }
+        l_run = __builtin_fmaf(l_run, alpha, ps);
+#pragma unroll
+        for (int j = 0; j < NDB; ++j) o[j] *= alpha;
+        m_run = m_new;
+
+        // O^T += V^T P^T
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int key = 8 * (i >> 2) + 4 * h + (i & 3);
+#pragma unroll
+            for (int j = 0; j < NDB; ++j)
+                o[j] = __builtin_amdgcn_mfma_f32_32x32x2f32(vt[key * LROW + 32 * j + c], s[i], o[j],
+                                                             0, 0, 0);
+            // V reads stay within a few k-steps of their MFMAs (hoisting
+            // them all would not fit the register file)
+            if ((i & 3) == 3) __builtin_amdgcn_sched_barrier(0);
+        }
+        // every wave is done with the other buffer (read in the previous
+        // tile, before the barrier that ended it)
+        if (t + 1 < nt) stage_store(buf ^ 1);
+        __syncthreads();
+    }
+
+    // ---- epilogue: lane (c, h) holds O^T rows 32 j + 8 r + 4 h .. + 3 of query c
+    const float l_tot = half_sum(l_run);
+    const float inv = 1.0f / l_tot;
+    if (qi < nq) {
+        float* orow = (float*)a.o + b * a.batch_stride + (int64_t)hd * D + qi * a.row_stride;
+#pragma unroll
+        for (int j = 0; j < NDB; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                *(float4*)(orow + 32 * j + 8 * r + 4 * h) =
+                    float4{o[j][4 * r] * inv, o[j][4 * r + 1] * inv, o[j][4 * r + 2] * inv,
+                           o[j][4 * r + 3] * inv};
+        if (a.lse != nullptr && h == 0) a.lse[bh * nq + qi] = m_run * a.scale + logf(l_tot);
     }
 }
 
@@ -736,7 +832,8 @@ void fa_fwd_f32_kernel(FaArgs a) {
 
 // Query rows one workgroup covers (the host sizes the grid with it).
 int flash_attn_rows_per_workgroup(bool bf16, int64_t head_dim) {
-    return bf16 ? 32 * FAD_WAVES : 256 / (int)(head_dim / 32);
+    (void)head_dim;
+    return bf16 ? 32 * FAD_WAVES : 32 * FA32_WAVES;
 }
 
 hipError_t launch_flash_attn(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -792,9 +889,15 @@ hipError_t launch_flash_attn(const void* q, const void* k, const void* v, void* 
         }
 #undef VX_FA
     } else {
-        const dim3 block(256);
-        if (head_dim == 128) hipLaunchKernelGGL(fa_fwd_f32_kernel<128>, grid, block, 0, st, a);
-        else hipLaunchKernelGGL(fa_fwd_f32_kernel<64>, grid, block, 0, st, a);
+        const dim3 block(64 * FA32_WAVES);
+        if (head_dim == 128 && a.has_pad)
+            hipLaunchKernelGGL((fa_fwd_f32_mfma_kernel<128, true>), grid, block, 0, st, a);
+        else if (head_dim == 128)
+            hipLaunchKernelGGL((fa_fwd_f32_mfma_kernel<128, false>), grid, block, 0, st, a);
+        else if (a.has_pad)
+            hipLaunchKernelGGL((fa_fwd_f32_mfma_kernel<64, true>), grid, block, 0, st, a);
+        else
+            hipLaunchKernelGGL((fa_fwd_f32_mfma_kernel<64, false>), grid, block, 0, st, a);
     }
     return hipGetLastError();
 }

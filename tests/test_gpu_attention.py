@@ -275,3 +275,45 @@ def test_widest_rows_the_host_accepts(gpu_lib, d):
     assert not torch.isnan(o).any().item()
     del q, k, v, o, lse
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("n,heads,d,batch,rope", [
+    (4096, 8, 128, 1, False), (3001, 4, 64, 2, False), (2000, 3, 128, 1, True),
+    (1555, 2, 64, 1, True),
+])
+def test_f32_mfma_at_size(gpu_lib, n, heads, d, batch, rope):
+    """fp32 attention (v_mfma_f32_32x32x2_f32 for both products) beyond the
+    tiny workload: every row of every head against the oracle at the fp32
+    bound, with ragged last tiles and, with RoPE, a text prefix and Q rotated
+    on load (K rotated by vx_rope3d_apply)."""
+    import torch
+    say(f"attn f32 mfma n={n} heads={heads} d={d} batch={batch} rope={rope}")
+    shape = (batch, n, heads, d)
+    q, k, v = (_rand(shape, "f32", 7000 + n + i) for i in range(3))
+    tq, tk, tv = dev(q), dev(k), dev(v)
+    split = (16, 24, 24) if d == 64 else (44, 42, 42)
+    prefix = 7
+    grid = None
+    if rope:
+        nv = n - prefix
+        grid = (1, 1, nv)
+        for tt in range(2, 12):
+            if nv % tt == 0:
+                grid = (tt, 1, nv // tt)
+                break
+        desc = binding.RopeDesc.of(grid, split, 10000.0, prefix)
+        binding.rope3d_apply(None, tk, desc)
+    o = torch.full_like(tq, float("nan"))
+    lse = torch.full((batch, heads, n), float("nan"), device="cuda")
+    binding.flash_attn_fwd(tq, tk, tv, o, lse, 0.0, desc if rope else None)
+    torch.cuda.synchronize()
+    og, lg = host(o), lse.cpu().numpy()
+    for b in range(batch):
+        if rope:
+            ref, rl = oracle.attention_rope(inputs.values(q[b]), inputs.values(k[b]),
+                                            inputs.values(v[b]), grid, split, 10000.0, prefix)
+        else:
+            ref, rl = oracle.attention(inputs.values(q[b]), inputs.values(k[b]),
+                                       inputs.values(v[b]))
+        check(og[b], ref, "f32", f"o[{b}]")
+        assert np.abs(lg[b] - rl).max() <= LSE_TOL["f32"]
