@@ -505,6 +505,11 @@ void fa_fwd_bf16_dma_kernel(FaArgs a) {
             const int kb2 = i / NKK, kk = i % NKK;
             f32x16_t& d = sb[nxt(kb2)];
             d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i % 3], qf[kk], kk == 0 ? negm : d, 0, 0, 0);
+            // nothing after the MFMA moves above it: otherwise the first
+            // group of a step may start with its exponentials and leave the
+            // MFMA unit idle at the step boundary (+0.2% at head_dim 128,
+            // +0.9% at 64, bit-identical)
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int e = 0; e < WPM; ++e) {
                 const int w = i * WPM + e;   // weights 2w, 2w+1: block (2w) / 16 of S(t)
