@@ -248,19 +248,21 @@ def test_large_rising_scores(gpu_lib, d, pattern):
     assert err.max() <= LSE_TOL["bf16"]
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("d", [64, 128])
-def test_widest_rows_the_host_accepts(gpu_lib, d):
+def test_widest_rows_the_host_accepts(gpu_lib, d, dtype):
     """heads * head_dim = 2^22, the most the host accepts: a token row is 8 MiB,
     so a key tile is 0.5 or 1 GiB and its buffer resource is clamped near the
-    2^31-byte limit; 130 tokens leave a ragged last tile.  Inputs are drawn on
-    the GPU (N(0,1), rounded to bf16); sampled heads, all rows, against the
-    oracle."""
+    2^31-byte limit (bf16); 130 tokens leave a ragged last tile.  Inputs are
+    drawn on the GPU (N(0,1), in the dtype); sampled heads, all rows, against
+    the oracle."""
     import torch
     heads, n = 2**22 // d, 130
-    say(f"attn widest rows d={d} heads={heads} n={n}")
+    say(f"attn widest rows {dtype} d={d} heads={heads} n={n}")
     g = torch.Generator(device="cuda")
     g.manual_seed(11 + d)
-    q, k, v = (torch.randn((1, n, heads, d), device="cuda", generator=g).to(torch.bfloat16)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    q, k, v = (torch.randn((1, n, heads, d), device="cuda", generator=g).to(tdt)
                for _ in range(3))
     o = torch.full_like(q, float("nan"))
     lse = torch.full((1, heads, n), float("nan"), device="cuda")
@@ -270,8 +272,8 @@ def test_widest_rows_the_host_accepts(gpu_lib, d):
     for h in picks:
         sl = lambda t: t[0, :, h:h + 1, :].float().cpu().numpy()
         ref, rl = oracle.attention(sl(q), sl(k), sl(v))
-        check(sl(o), ref, "bf16", f"o head {h}")
-        assert np.abs(lse[0, h].cpu().numpy() - rl[0]).max() <= LSE_TOL["bf16"]
+        check(sl(o), ref, dtype, f"o head {h}")
+        assert np.abs(lse[0, h].cpu().numpy() - rl[0]).max() <= LSE_TOL[dtype]
     assert not torch.isnan(o).any().item()
     del q, k, v, o, lse
     torch.cuda.empty_cache()
