@@ -397,7 +397,9 @@ void fa_fwd_bf16_dma_kernel(FaArgs a) {
     };
     // V^T fragment (db, kk), half r: keys kk*16 + 4 (2r + g) + s / 4 (the
     // S^T accumulator's key order), columns db*32 + 16 hh + 4 (s & 3)..+3,
-    // with s = lane & 15, hh = (lane >> 4) & 1
+    // with s = lane & 15, hh = (lane >> 4) & 1.  Fragments are numbered in
+    // the order the P V product takes them: 16-key step kk outer, 32-column
+    // block db inner, so consecutive MFMAs go to different accumulators.
     uint32_t voff[2][NDB];
     {
         const int s_ = lane & 15, hh = (lane >> 4) & 1;
@@ -411,7 +413,7 @@ void fa_fwd_bf16_dma_kernel(FaArgs a) {
             }
     }
     auto vfrag = [&](int jv, int i) {   // V buffer jv (compile-time), fragment i
-        const int db = i / KS, kk = i % KS;
+        const int db = i % NDB, kk = i / NDB;
         const bf16x4_t lo = lds_read_tr(lds + voff[0][db] + (jv * TILEB + kk * 16 * ROWB));
         const bf16x4_t hi = lds_read_tr(lds + voff[1][db] + (jv * TILEB + kk * 16 * ROWB));
         return bf16x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
@@ -524,10 +526,10 @@ void fa_fwd_bf16_dma_kernel(FaArgs a) {
             if (i + 1 == NX) vf[1] = vfrag(j0, 1);
             __builtin_amdgcn_sched_barrier(0);
         }
-        bf16x8_t pb[KS];
-#pragma unroll
-        for (int kk = 0; kk < KS; ++kk)
-            pb[kk] = __builtin_bit_cast(bf16x8_t, u32x4_t{pw[4 * kk], pw[4 * kk + 1], pw[4 * kk + 2], pw[4 * kk + 3]});
+        // P(t) words 4 kk .. 4 kk + 3 as the B operand of 16-key step kk
+        auto pb = [&](int kk) {
+            return __builtin_bit_cast(bf16x8_t, u32x4_t{pw[4 * kk], pw[4 * kk + 1], pw[4 * kk + 2], pw[4 * kk + 3]});
+        };
         // ---- Y: O += V(t)^T P(t)  ||  row sum of P(t); row max of S(t+1);
         // first K(t+2) fragments
         const bf16x2_t one = {(__bf16)1.0f, (__bf16)1.0f};
@@ -551,7 +553,7 @@ void fa_fwd_bf16_dma_kernel(FaArgs a) {
                 kf[1] = kfrag(j2, 1);
             }
             if (i + 2 < NY) vf[(i + 2) % 3] = vfrag(j0, i + 2);
-            acc[i / KS] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i % 3], pb[i % KS], acc[i / KS], 0, 0, 0);
+            acc[i % NDB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i % 3], pb(i / NDB), acc[i % NDB], 0, 0, 0);
             // V(t+2) where V(t-1) was, after the barrier, one request every
             // NY / 2 / NI groups
             if (i >= NY / 2 && (i - NY / 2) % (NY / 2 / NI) == 0)
@@ -578,8 +580,9 @@ void fa_fwd_bf16_dma_kernel(FaArgs a) {
             mask_tile(tm, tl.at(t + 1));
             mx_next = row_max(tm);
         }
-        // ---- lazy rescale for S(t+1) (rare after the first tiles)
-        if (t + 1 < nt && __builtin_amdgcn_ballot_w64(mx_next > lazy) != 0) {
+        // ---- lazy rescale for S(t+1) (rare after the first tiles; laid out
+        // off the straight-line path, so a step without it takes no branch)
+        if (__builtin_expect(t + 1 < nt && __builtin_amdgcn_ballot_w64(mx_next > lazy) != 0, 0)) {
             const float delta = fmaxf(mx_next, 0.f);
             const float alpha = weight(-delta);
             m_ref += delta;
