@@ -9,8 +9,8 @@
 // HBM-bound: each rotated row of Q and K is read and written once.  A
 // workgroup owns TPB consecutive tokens.  It evaluates cos/sin of the
 // head_dim/2 angles of each token into LDS (angles are shared by every head
-// and by Q and K, so they cost one evaluation per token and pair) while the
-// first loads of the tokens' rows are in flight, then streams the 16-byte
+// and by Q and K, so they cost one evaluation per token and pair) after
+// issuing the first loads of the tokens' rows, then streams the 16-byte
 // chunks of the Q and K rows, consecutive lanes on consecutive chunks, each
 // thread with several loads in flight; rows far larger than the memory-side
 // cache are read and written with non-temporal accesses.  With adjacent pairs (pairing 0) both elements of
@@ -57,8 +57,11 @@ __device__ __forceinline__ void stream_store(uint4* p, const uint4& v) {
 // them BATCH at a time: all loads of a batch are issued before any chunk is
 // rotated and stored, so each thread keeps BATCH 16-byte loads in flight (a
 // load issued after a store to another chunk could not be moved above it).
-// The first batch is loaded before the angles are evaluated, so the sin/cos
-// work runs under those loads.  Text-prefix rows are read but never written.
+// The first batch is loaded before the angles are evaluated.  Each angle's
+// pair frequency is itself a load issued after that batch, so the
+// evaluation starts once the batch has landed (loads complete in issue
+// order); fetching the frequencies first, so the evaluation runs under the
+// batch, measured no faster.  Text-prefix rows are read but never written.
 // BATCH is 8 when every thread has at least 8 chunks (wide token rows), else
 // 4: eight loads in flight need 87 VGPRs (5 waves per SIMD) against 56 (8
 // waves), and rows of a few heads gain more from occupancy than from depth.
