@@ -581,7 +581,7 @@ void fa_fwd_bf16_dma_kernel(FaArgs a) {
             mx_next = row_max(tm);
         }
         // ---- lazy rescale for S(t+1) (rare after the first tiles; laid out
-        // off the straight-line path, so a step without it takes no branch)
+        // off the straight-line path, so a step that skips it does not jump)
         if (__builtin_expect(t + 1 < nt && __builtin_amdgcn_ballot_w64(mx_next > lazy) != 0, 0)) {
             const float delta = fmaxf(mx_next, 0.f);
             const float alpha = weight(-delta);
