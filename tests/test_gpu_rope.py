@@ -38,11 +38,12 @@ def test_workload(gpu_lib, name):
 
 
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("name", ["large_sp8", "mixed_sp4"])
+@pytest.mark.parametrize("name", list(configs.SP_WORKLOADS))
 def test_sp_share_workload(gpu_lib, name):
-    """One GPU's share under sequence parallelism: all 75,600 (85,906) tokens
-    with 5 (12) heads, so a token row is narrow and a workgroup spans 32
-    tokens; every token of Q and K against the oracle."""
+    """One GPU's share under sequence parallelism: all tokens of the grid with
+    H/P heads (5 to 24), so a token row is narrow and each thread of a
+    workgroup has only a few chunks; every token of Q and K against the
+    oracle."""
     import torch
     wl = configs.SP_WORKLOADS[name]
     say(f"rope sp share {name}: N={wl.n_tokens} H={wl.heads} d={wl.head_dim}")
